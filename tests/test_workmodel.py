@@ -1,0 +1,51 @@
+"""Pin the byte and flop models used for roofline pricing to the pages' printed numbers."""
+
+import importlib.util
+import os
+
+import pytest
+
+_spec = importlib.util.spec_from_file_location(
+    "workmodel", os.path.join(os.path.dirname(__file__), "..", "attention_gqa_flash_02_amd", "workmodel.py"))
+wm = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(wm)
+
+
+def test_score_matrix_at_8192_is_134_mb():
+    # "Attention kernels", standard attention: N = 8192 gives ~67M scores, ~134 MB per head in BF16
+    assert 8192 * 8192 == 67_108_864
+    assert wm.score_matrix_bytes(8192, 2) == 134_217_728
+
+
+def test_decode_intensity_is_one_times_group():
+    # "Attention kernels", prefill and decode: decode intensity is about 1, times the group size with GQA
+    assert wm.decode_intensity(1, 2) == 1.0
+    assert wm.decode_intensity(4, 2) == 4.0
+    assert wm.decode_intensity(16, 2) == 16.0
+
+
+def test_kv_memory_ratio_mha_gqa_mqa():
+    # "Optimization 1", 2.2: MHA 100% / GQA 50% / MQA 25% (4 query heads: 4, 2, 1 KV heads)
+    full = wm.kv_bytes([1000], 4, 128, 2)
+    assert [wm.kv_bytes([1000], h, 128, 2) / full for h in (4, 2, 1)] == [1.0, 0.5, 0.25]
+
+
+def test_kv_cache_formula_per_layer():
+    # talk summary 37:00: kv_cache_size_per_seq = S * (K*H) * L * 2 * 2
+    assert wm.kv_cache_bytes_per_seq(4096, 8, 128, 32, 2) == 4096 * (8 * 128) * 32 * 2 * 2
+    assert wm.kv_bytes([4096], 8, 128, 2) == wm.kv_cache_bytes_per_seq(4096, 8, 128, 1, 2)
+
+
+@pytest.mark.parametrize("lq,lk", [(1, 1), (5, 5), (3, 10), (10, 3), (8192, 8192), (2048, 20000)])
+def test_visible_pairs_bruteforce(lq, lk):
+    if lq * lk <= 10_000:
+        brute = sum(1 for i in range(lq) for j in range(lk) if j <= lk - lq + i)
+    else:
+        brute = sum(min(lk, max(0, lk - lq + i + 1)) for i in range(lq))
+    assert wm.visible_pairs(lq, lk, True) == brute
+    assert wm.visible_pairs(lq, lk, False) == lq * lk
+
+
+def test_c3_flops():
+    assert wm.prefill_flops([8192] * 4, [8192] * 4, 32, 128) == 4 * 128 * 32 * 4 * (8192 * 8193 // 2)
+    assert wm.prefill_flops([8192] * 4, [8192] * 4, 32, 128) == 2_199_291_691_008
