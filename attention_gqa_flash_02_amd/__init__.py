@@ -1,0 +1,196 @@
+"""Exact grouped-query softmax attention over a KV cache on AMD MI355X (gfx950).
+
+A thin Python binding of the C ABI declared in include/attn_gqa.h: each
+function below has the name of the C entry point it calls and only marshals
+arguments (torch tensors -> device pointers and sizes, the current HIP stream).
+Every step of the computation runs in the HIP kernels of lib/libattn_gqa.so;
+there is no fallback: if the library is not built, calls raise.
+
+PyTorch is used for device memory (outputs, workspace) and streams only.
+"""
+
+import torch
+
+from . import _lib
+from .workmodel import visible_pairs, prefill_flops, kv_bytes
+
+__all__ = [
+    "AttnError",
+    "ATTN_KV_BF16",
+    "ATTN_KV_FP8_E4M3FN",
+    "attn_status_string",
+    "attn_prefill_varlen",
+    "attn_decode_num_splits",
+    "attn_decode_workspace_bytes",
+    "attn_decode_paged",
+    "attn_varlen_workspace_bytes",
+    "attn_varlen_paged",
+    "library_path",
+]
+
+ATTN_KV_BF16 = 0
+ATTN_KV_FP8_E4M3FN = 1
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = int(status)
+        super().__init__(f"{where}: {attn_status_string(status)}")
+
+
+def library_path():
+    return _lib.LIB_PATH
+
+
+def attn_status_string(status):
+    return _lib.load().attn_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(t, name, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _kv_dtype(cache):
+    if cache.dtype == torch.bfloat16:
+        return ATTN_KV_BF16
+    if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return ATTN_KV_FP8_E4M3FN
+    raise TypeError(f"unsupported KV cache dtype {cache.dtype}")
+
+
+def attn_prefill_varlen(q, k, v, cu_seqlens, causal, scale, out=None, lse=None, max_seqlen=None,
+                        return_lse=True, stream=None):
+    """q [T, Hq, D], k/v [T, Hkv, D] bf16; cu_seqlens int32 [B+1] on the same device.
+    Returns (out [T, Hq, D] bf16, lse [T, Hq] fp32 or None)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, torch.bfloat16, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    if max_seqlen is None:
+        cu = cu_seqlens.cpu()
+        max_seqlen = int((cu[1:] - cu[:-1]).max()) if cu.numel() > 1 else 0
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((total, hq), dtype=torch.float32, device=dev)
+    st = _lib.load().attn_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), int(bool(causal)), float(scale), _ptr(out), _ptr(lse),
+        cu_seqlens.numel() - 1, total, int(max_seqlen), hq, hkv, d, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_prefill_varlen")
+    return out, lse
+
+
+def attn_decode_num_splits(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, requested=0):
+    return int(_lib.load().attn_decode_num_splits(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
+                                                  requested))
+
+
+def attn_decode_workspace_bytes(num_seqs, num_kv_heads, head_dim, num_splits):
+    return int(_lib.load().attn_decode_workspace_bytes(num_seqs, num_kv_heads, head_dim, num_splits))
+
+
+def attn_varlen_workspace_bytes(num_seqs, num_kv_heads, head_dim, num_splits):
+    return int(_lib.load().attn_varlen_workspace_bytes(num_seqs, num_kv_heads, head_dim, num_splits))
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return workspace
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale=None, v_scale=None,
+                      out=None, lse=None, num_splits=0, workspace=None, return_lse=True, stream=None):
+    """q [B, Hq, D] bf16; k_cache [N, Hkv, bs, D], v_cache [N, Hkv, D, bs] (bf16, or uint8 e4m3fn codes
+    with k_scale/v_scale fp32 [Hkv]); block_table int32 [B, max_blocks]; seq_lens int32 [B]."""
+    dev = q.device
+    _check(q, "q", torch.bfloat16, dev)
+    kvt = _kv_dtype(k_cache)
+    if _kv_dtype(v_cache) != kvt:
+        raise TypeError("k_cache and v_cache must have the same dtype")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    _check(block_table, "block_table", torch.int32, dev)
+    _check(seq_lens, "seq_lens", torch.int32, dev)
+    if kvt == ATTN_KV_FP8_E4M3FN:
+        _check(k_scale, "k_scale", torch.float32, dev)
+        _check(v_scale, "v_scale", torch.float32, dev)
+    b, hq, d = q.shape
+    nblk, hkv, bs, _ = k_cache.shape
+    maxblk = block_table.shape[1]
+    splits = attn_decode_num_splits(b, hkv, bs, maxblk, num_splits)
+    ws = _workspace(attn_decode_workspace_bytes(b, hkv, d, splits), dev, workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((b, hq), dtype=torch.float32, device=dev)
+    st = _lib.load().attn_decode_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), kvt, _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), b, hq, hkv, d, bs, nblk, maxblk, splits,
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_paged")
+    return out, lse
+
+
+def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k, causal, scale,
+                      k_scale=None, v_scale=None, out=None, lse=None, max_q_len=None, num_splits=0,
+                      workspace=None, return_lse=True, stream=None):
+    """Mixed varlen batch (prefill chunks over cached prefixes and decode tokens) over a paged cache."""
+    dev = q.device
+    _check(q, "q", torch.bfloat16, dev)
+    kvt = _kv_dtype(k_cache)
+    if _kv_dtype(v_cache) != kvt:
+        raise TypeError("k_cache and v_cache must have the same dtype")
+    _check(block_table, "block_table", torch.int32, dev)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _check(seq_lens_k, "seq_lens_k", torch.int32, dev)
+    if kvt == ATTN_KV_FP8_E4M3FN:
+        _check(k_scale, "k_scale", torch.float32, dev)
+        _check(v_scale, "v_scale", torch.float32, dev)
+    tq, hq, d = q.shape
+    nblk, hkv, bs, _ = k_cache.shape
+    b = seq_lens_k.numel()
+    maxblk = block_table.shape[1]
+    if max_q_len is None:
+        cu = cu_seqlens_q.cpu()
+        max_q_len = int((cu[1:] - cu[:-1]).max()) if cu.numel() > 1 else 0
+    splits = attn_decode_num_splits(b, hkv, bs, maxblk, num_splits)
+    ws = _workspace(attn_varlen_workspace_bytes(b, hkv, d, splits), dev, workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=dev)
+    st = _lib.load().attn_varlen_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), kvt, _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        _ptr(cu_seqlens_q), _ptr(seq_lens_k), int(bool(causal)), float(scale), _ptr(out), _ptr(lse),
+        b, tq, int(max_q_len), hq, hkv, d, bs, nblk, maxblk, splits, _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_varlen_paged")
+    return out, lse

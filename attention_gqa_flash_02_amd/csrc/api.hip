@@ -1,0 +1,214 @@
+// C-ABI entry points: argument validation, partition planning and dispatch.
+// Validation happens before any HIP call, so an invalid call touches nothing.
+#include <atomic>
+#include <climits>
+#include <cmath>
+
+#include "../../include/attn_gqa.h"
+#include "launch.h"
+
+namespace attn {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+static bool supported_block_size(int bs) {
+  return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256;
+}
+
+static int gcd_int(int a, int b) {
+  while (b) {
+    int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Partition length for a given count: a multiple of 64 keys (one wave chunk).
+static int split_tokens_for(int max_len, int num_splits) {
+  int per = (max_len + num_splits - 1) / num_splits;
+  per = ((per + 63) / 64) * 64;
+  return per > 0 ? per : 64;
+}
+
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" {
+
+const char* attn_status_string(attn_status status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_NULL: return "ATTN_ERR_NULL: a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE: inconsistent or non-positive sizes";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: head_dim, block_size or kv dtype not supported";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
+    case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: the HIP runtime rejected the launch";
+    default: return "ATTN_ERR_UNKNOWN";
+  }
+}
+
+attn_status attn_prefill_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                int32_t causal, float scale, void* out, float* lse, int32_t num_seqs,
+                                int32_t total_tokens, int32_t max_seqlen, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, void* stream) {
+  if (!q || !k || !v || !cu_seqlens || !out) return ATTN_ERR_NULL;
+  if (num_seqs <= 0 || total_tokens < 0 || max_seqlen < 0 || max_seqlen > total_tokens ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      (causal != 0 && causal != 1) || !std::isfinite(scale))
+    return ATTN_ERR_SHAPE;
+  if (head_dim != 128 && head_dim != 256) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)total_tokens * num_q_heads * head_dim > (long long)INT_MAX * 8) return ATTN_ERR_SHAPE;
+  if (total_tokens == 0 || max_seqlen == 0) return ATTN_OK;
+
+  PrefillParams p{};
+  p.q = static_cast<const bf16*>(q);
+  p.k = static_cast<const bf16*>(k);
+  p.v = static_cast<const bf16*>(v);
+  p.cu_seqlens = cu_seqlens;
+  p.out = static_cast<bf16*>(out);
+  p.lse = lse;
+  p.scale = scale;
+  p.num_seqs = num_seqs;
+  p.Hq = num_q_heads;
+  p.Hkv = num_kv_heads;
+  p.g = num_q_heads / num_kv_heads;
+  p.hpw = gcd_int(p.g, 4);
+  p.causal = causal;
+  hipError_t e = launch_prefill(p, head_dim, max_seqlen, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t requested) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || requested < 0)
+    return 0;
+  const long long max_len = (long long)max_blocks_per_seq * block_size;
+  const int max_chunks = (int)((max_len + 63) / 64);
+  int s;
+  if (requested > 0) {
+    s = requested;
+  } else {
+    // Aim for about four partition workgroups per compute unit, each at least 256 keys long.
+    const long long units = (long long)num_seqs * num_kv_heads;
+    const long long target = 4LL * device_cu_count();
+    long long want = (target + units - 1) / units;
+    const long long cap = (max_len + 255) / 256;
+    if (want > cap) want = cap;
+    s = (int)(want < 1 ? 1 : want);
+  }
+  if (s > max_chunks) s = max_chunks;
+  if (s > 4096) s = 4096;
+  return s < 1 ? 1 : s;
+}
+
+size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_splits) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_splits <= 1) return 0;
+  return (size_t)num_seqs * num_kv_heads * num_splits * 16 * ((size_t)head_dim + 1) * sizeof(float);
+}
+
+static attn_status validate_paged(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                                  const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                  const int32_t* seq_lens, const void* out, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                  int32_t num_splits) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return ATTN_ERR_NULL;
+  if (kv_dtype != ATTN_KV_BF16 && kv_dtype != ATTN_KV_FP8_E4M3FN) return ATTN_ERR_UNSUPPORTED;
+  if (kv_dtype == ATTN_KV_FP8_E4M3FN && (!k_scale || !v_scale)) return ATTN_ERR_NULL;
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || num_splits < 0)
+    return ATTN_ERR_SHAPE;
+  if (head_dim != 128 && head_dim != 256) return ATTN_ERR_UNSUPPORTED;
+  if (!supported_block_size(block_size)) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size > INT_MAX / 2) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                              const float* k_scale, const float* v_scale, const int32_t* block_table,
+                              const int32_t* seq_lens, float scale, void* out, float* lse,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t num_splits, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  attn_status st = validate_paged(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_table, seq_lens,
+                                  out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  num_blocks, max_blocks_per_seq, num_splits);
+  if (st != ATTN_OK) return st;
+  if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
+  const int g = num_q_heads / num_kv_heads;
+  if (g > 16) return ATTN_ERR_UNSUPPORTED;
+  const int S = attn_decode_num_splits(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, num_splits);
+  const size_t need = attn_decode_workspace_bytes(num_seqs, num_kv_heads, head_dim, S);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+
+  PagedParams p{};
+  p.q = static_cast<const bf16*>(q);
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_table = block_table;
+  p.seq_lens_k = seq_lens;
+  p.cu_seqlens_q = nullptr;
+  p.out = static_cast<bf16*>(out);
+  p.lse = lse;
+  const size_t ws_o_elems = (size_t)num_seqs * num_kv_heads * S * 16 * head_dim;
+  p.ws_o = need ? static_cast<float*>(workspace) : nullptr;
+  p.ws_lse = need ? static_cast<float*>(workspace) + ws_o_elems : nullptr;
+  p.scale = scale;
+  p.num_seqs = num_seqs;
+  p.Hq = num_q_heads;
+  p.Hkv = num_kv_heads;
+  p.g = g;
+  p.bs = block_size;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_splits = S;
+  p.split_tokens = split_tokens_for(max_blocks_per_seq * block_size, S);
+  p.causal = 1;
+  hipError_t e = launch_decode(p, head_dim, kv_dtype == ATTN_KV_BF16 ? KV_BF16 : KV_FP8, g,
+                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+size_t attn_varlen_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_splits) {
+  return attn_decode_workspace_bytes(num_seqs, num_kv_heads, head_dim, num_splits);
+}
+
+attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                              const float* k_scale, const float* v_scale, const int32_t* block_table,
+                              const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t causal,
+                              float scale, void* out, float* lse, int32_t num_seqs, int32_t total_q,
+                              int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = validate_paged(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_table, seq_lens_k,
+                                  out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  num_blocks, max_blocks_per_seq, num_splits);
+  if (st != ATTN_OK) return st;
+  if (!cu_seqlens_q) return ATTN_ERR_NULL;
+  if (total_q < 0 || max_q_len < 0 || max_q_len > total_q || (causal != 0 && causal != 1) ||
+      !std::isfinite(scale))
+    return ATTN_ERR_SHAPE;
+  (void)workspace;
+  (void)workspace_bytes;
+  (void)stream;
+  (void)lse;
+  return ATTN_ERR_UNSUPPORTED;  // mixed launch not built yet
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+/*
+ * attn_gqa.h -- exact grouped-query softmax attention over a KV cache for AMD
+ * MI355X (gfx950). C ABI: plain pointers and sizes, no framework types.
+ *
+ * What is computed (every entry point): for request b, query head h and query
+ * row i, with kv head = h / (num_q_heads / num_kv_heads) (contiguous groups,
+ * "Optimization 1: batching and attention", sections 2.2 and 2.4):
+ *     s_ij  = scale * <q_i, k_j>                 over the keys j row i may see
+ *     out_i = sum_j softmax(s_i)_j * v_j         ("Attention kernels", section
+ *                                                 "Memory round trips of standard attention")
+ *     lse_i = ln sum_j exp(s_ij)                 (natural log, scale included)
+ * The result is exact softmax attention (no approximation): the kernels tile
+ * the key axis and keep running row statistics (online softmax, "Attention
+ * kernels", section "FlashAttention"); they never write the score matrix.
+ * Causal masking is bottom-right aligned: row i of a request with Lq new rows
+ * and Lk keys sees keys j <= Lk - Lq + i. A row that sees no key gets out = 0
+ * and lse = -inf.
+ *
+ * Conventions shared by all calls:
+ *   - Every pointer argument is DEVICE memory allocated and owned by the caller
+ *     (except where stated). The library allocates nothing, frees nothing,
+ *     never synchronises the stream and never changes the current device.
+ *   - Inputs are read only. out / lse are overwritten in full (every row of
+ *     every head); they must not alias any input or the workspace.
+ *   - bf16 means IEEE bfloat16 (2 bytes). fp8 means OCP e4m3fn codes (1 byte):
+ *     bias 7, no infinities, max 448; the value is code * per-head scale.
+ *   - Layouts are row-major with the last index fastest:
+ *       q, out   [tokens, num_q_heads, head_dim]
+ *       lse      [tokens, num_q_heads]                  fp32
+ *       k, v     [tokens, num_kv_heads, head_dim]       (contiguous prefill)
+ *       k_cache  [num_blocks, num_kv_heads, block_size, head_dim]
+ *       v_cache  [num_blocks, num_kv_heads, head_dim, block_size]  (tokens innermost)
+ *       block_table [num_seqs, max_blocks_per_seq] int32: logical block i of
+ *       request b lives in physical block block_table[b][i]; token t is slot
+ *       t % block_size of logical block t / block_size ("Optimization 1",
+ *       section 3.4 PagedAttention; "Attention kernels", section "Paged KV and kernels").
+ *   - head_dim must be 128 or 256; num_q_heads must be a multiple of
+ *     num_kv_heads; block_size must be 16, 32, 64, 128 or 256.
+ *   - stream is a hipStream_t (NULL = the default stream). Calls return once
+ *     the work is enqueued; results are valid after the stream synchronises.
+ *   - Argument validation is synchronous and happens before anything is
+ *     launched; on any error nothing is launched and nothing is written.
+ *     Device-resident values (cu_seqlens, seq_lens, block-table entries) are
+ *     NOT validated: they are the caller's contract (monotone cu_seqlens,
+ *     0 <= seq_lens[b] <= max_blocks_per_seq * block_size, table entries in
+ *     [0, num_blocks) for every block a request uses).
+ */
+#ifndef ATTN_GQA_H
+#define ATTN_GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t attn_status;
+
+#define ATTN_OK 0
+#define ATTN_ERR_NULL 1         /* a required pointer is NULL */
+#define ATTN_ERR_SHAPE 2        /* counts <= 0, Hq % Hkv != 0, inconsistent sizes */
+#define ATTN_ERR_UNSUPPORTED 3  /* head_dim, block_size or kv dtype not supported */
+#define ATTN_ERR_WORKSPACE 4    /* workspace NULL or smaller than required */
+#define ATTN_ERR_LAUNCH 5       /* the HIP runtime reported an error at launch */
+
+#define ATTN_KV_BF16 0
+#define ATTN_KV_FP8_E4M3FN 1
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* attn_status_string(attn_status status);
+
+/*
+ * Varlen prefill over contiguous K/V ("Attention kernels", section
+ * "FlashAttention"; the varlen batch: section "Paged KV and kernels").
+ * Request b owns rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of q, k, v, out, lse
+ * and attends within itself (Lq = Lk = its length).
+ *   q [total_tokens, num_q_heads, head_dim] bf16; k, v [total_tokens, num_kv_heads, head_dim] bf16
+ *   cu_seqlens [num_seqs + 1] int32 (device), cu_seqlens[0] = 0, cu_seqlens[num_seqs] = total_tokens
+ *   causal: 0 or 1; scale: score multiplier (e.g. 1/sqrt(head_dim))
+ *   out [total_tokens, num_q_heads, head_dim] bf16 (round to nearest even)
+ *   lse [total_tokens, num_q_heads] fp32, or NULL to skip it
+ *   max_seqlen: an upper bound on every request's length (sizes the grid)
+ * Needs no workspace: nothing but out and lse is written.
+ */
+attn_status attn_prefill_varlen(const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens, int32_t causal, float scale,
+                                void* out, float* lse,
+                                int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                void* stream);
+
+/*
+ * Number of KV partitions a paged decode call will use (split-KV, "Attention
+ * kernels", section "Prefill and decode attention"). requested > 0 is
+ * returned unchanged (clamped to the number of 16-token tiles of the longest
+ * request); requested == 0 picks one from the batch shape and the device's
+ * compute-unit count. Returns 0 on invalid sizes.
+ */
+int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t requested);
+
+/*
+ * Workspace bytes a paged decode / varlen-paged call needs for num_splits
+ * (resolved, >= 1) partitions: per (request, kv head, partition) a block of
+ * 16 rows x head_dim fp32 partial outputs plus 16 fp32 partial LSEs.
+ * 0 when num_splits == 1 (no partials are written).
+ */
+size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_splits);
+
+/*
+ * Paged decode: one query token per request over its paged KV cache.
+ * Each KV head is read once for all num_q_heads / num_kv_heads query heads of
+ * its group ("Attention kernels", section "Prefill and decode attention"); the
+ * key axis is cut into num_splits partitions of
+ *   C = roundup(ceil(max_blocks_per_seq * block_size / num_splits), 16) tokens,
+ * partition s covering keys [s*C, min((s+1)*C, seq_lens[b])), and the
+ * partitions are merged with their log-sum-exps.
+ *   q [num_seqs, num_q_heads, head_dim] bf16 (the newest token of each request)
+ *   k_cache, v_cache: see the layouts above; kv_dtype ATTN_KV_BF16 or ATTN_KV_FP8_E4M3FN
+ *   k_scale, v_scale [num_kv_heads] fp32 per-head dequantisation scales (fp8 only; ignored for bf16)
+ *   block_table [num_seqs, max_blocks_per_seq] int32; seq_lens [num_seqs] int32 =
+ *   number of cached tokens INCLUDING the current one (0 gives out 0, lse -inf)
+ *   out [num_seqs, num_q_heads, head_dim] bf16; lse [num_seqs, num_q_heads] fp32 or NULL
+ *   num_splits: 0 = automatic (attn_decode_num_splits), else the partition count
+ *   workspace: device scratch of >= attn_decode_workspace_bytes(...) bytes
+ *   (may be NULL when that is 0); its contents on entry do not matter.
+ * Requires num_q_heads / num_kv_heads <= 16.
+ */
+attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                              int32_t kv_dtype, const float* k_scale, const float* v_scale,
+                              const int32_t* block_table, const int32_t* seq_lens, float scale,
+                              void* out, float* lse,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Mixed varlen batch over a paged cache in one attention launch ("Attention
+ * kernels", section "Paged KV and kernels": prefill chunks and decode requests
+ * of different lengths in one step). Request b owns query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and seq_lens_k[b] cached keys, its
+ * own new tokens being the last Lq of them (a prefill chunk over a cached
+ * prefix, or a decode token). Requests whose Lq * (num_q_heads/num_kv_heads)
+ * is at most 16 run on the split-KV decode path (num_splits partitions, as in
+ * attn_decode_paged); the others run on the tiled prefill path.
+ *   q, out [total_q, num_q_heads, head_dim] bf16; lse [total_q, num_q_heads] fp32 or NULL
+ *   causal: 0 or 1 (bottom-right aligned)
+ *   workspace: >= attn_varlen_workspace_bytes(...) bytes of device scratch.
+ */
+size_t attn_varlen_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_splits);
+
+attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_cache,
+                              int32_t kv_dtype, const float* k_scale, const float* v_scale,
+                              const int32_t* block_table, const int32_t* cu_seqlens_q,
+                              const int32_t* seq_lens_k, int32_t causal, float scale,
+                              void* out, float* lse,
+                              int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t num_splits, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_GQA_H */
