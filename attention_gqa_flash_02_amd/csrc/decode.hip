@@ -9,11 +9,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(PagedParams p) {
   decode_unit<D, KVT>(p, blockIdx.z, blockIdx.y, blockIdx.x, reinterpret_cast<float*>(smem_raw));
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(PagedParams p) {
-  merge_unit<D>(p, blockIdx.x, blockIdx.y);
-}
-
 template <int D, int KVT>
 static hipError_t launch_decode_t(const PagedParams& p, int rows_max, hipStream_t stream) {
   const size_t lds = (128 + 4 * (size_t)rows_max * D) * sizeof(float);
@@ -27,9 +22,6 @@ static hipError_t launch_decode_t(const PagedParams& p, int rows_max, hipStream_
   }
   dim3 grid(p.num_splits, p.Hkv, p.num_seqs);
   hipLaunchKernelGGL((decode_split_kernel<D, KVT>), grid, dim3(256), lds, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.num_splits <= 1) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(p.num_seqs, p.Hkv), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

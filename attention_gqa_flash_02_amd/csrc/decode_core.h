@@ -42,9 +42,13 @@ struct PagedParams {
   float* lse;                  // [Tq, Hq] or nullptr
   float* ws_o;                 // [B, Hkv, S, 16, D] partial outputs (normalised)
   float* ws_lse;               // [B, Hkv, S, 16] partial natural-log LSEs
+  unsigned* counters;          // [B, Hkv] finished-partition counters (zero between calls)
   float scale;
   int num_seqs, Hq, Hkv, g, bs, max_blocks, num_splits, split_tokens, causal;
 };
+
+template <int D>
+__device__ void merge_unit(const PagedParams& p, int b, int kvh);
 
 // Rows of a request on this path: r -> (new token r / g, query head kvh*g + r % g).
 template <int D, int KVT>
@@ -286,12 +290,26 @@ __device__ __forceinline__ void decode_unit(const PagedParams& p, int b, int kvh
                 so[(3 * R + r) * D + d];
     }
     if (wave == 0 && qd == 0 && j < R) p.ws_lse[unit * 16 + j] = row_lse;
+    // The last partition of this (request, kv head) to finish merges all of them. atomicInc
+    // wraps at n_splits_b - 1, so the counter is back at zero once every partition has counted.
+    __threadfence();
+    __syncthreads();
+    int* flag = reinterpret_cast<int*>(lds);
+    if (tid == 0) {
+      const unsigned old = atomicInc(p.counters + (size_t)b * p.Hkv + kvh, (unsigned)(n_splits_b - 1));
+      *flag = (old == (unsigned)(n_splits_b - 1));
+    }
+    __syncthreads();
+    if (*flag) {
+      __threadfence();
+      merge_unit<D>(p, b, kvh);
+    }
   }
 }
 
 // Merge of the partitions of one (request, kv head): natural-log LSE weights.
 template <int D>
-__device__ __forceinline__ void merge_unit(const PagedParams& p, int b, int kvh) {
+__device__ void merge_unit(const PagedParams& p, int b, int kvh) {
   const int len = p.seq_lens_k[b];
   const int q0 = p.cu_seqlens_q ? p.cu_seqlens_q[b] : b;
   const int qlen = p.cu_seqlens_q ? (p.cu_seqlens_q[b + 1] - q0) : 1;

@@ -1,0 +1,270 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+A step is one call of the paged GQA decode on the batch-32 workload (32 query /
+8 KV heads, head dim 128, bf16 KV in 16-token blocks with shuffled pages,
+lengths uniform in [1024, 8192]): split-KV partitions + LSE merge in one
+launch. `value` is KV bytes read per second over the timed steps (inputs
+resident in HBM; the KV cache is rotated over copies so that no step finds it
+in the 256 MB last-level cache). The same run also times the causal varlen
+prefill (4 x 8192 tokens, 32/8 heads, D 128) and the long-context split-KV
+decode (2 x 131072 tokens, 32/2 heads, 64-token blocks), reports each against
+its roofline, checks sampled outputs against the fp64 oracle, and times the
+oracle itself on the host cores (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 4096 flop/clk x 2.4 GHz)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--splits", type=int, default=0, help="decode partitions (0 = library choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="time only the headline decode workload")
+    ap.add_argument("--quick", action="store_true", help="skip the parity samples")
+    return ap.parse_args()
+
+
+def time_steps(fns, steps, warmup):
+    """Run fns round-robin: warmup untimed, then `steps` timed between synchronisations.
+    Returns (wall ms per step, per-call event durations in ms)."""
+    import torch
+    n = len(fns)
+    for i in range(warmup):
+        fns[i % n]()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fns[i % n]()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, durs
+
+
+def rotate_paged(case, copies):
+    """Independent copies of the KV cache (same contents, different addresses)."""
+    out = [(case.k_cache, case.v_cache)]
+    for _ in range(copies - 1):
+        out.append((case.k_cache.clone(), case.v_cache.clone()))
+    return out
+
+
+def decode_section(lib, case, splits, steps, warmup, label):
+    import torch
+    from attention_gqa_flash_02_amd import workmodel
+    kv_bytes = workmodel.kv_bytes(case.kv_lens, case.num_kv_heads, case.head_dim,
+                                  2 if case.kv_format == "bf16" else 1)
+    copies = max(2, math.ceil(3 * 256e6 / kv_bytes) + 1)
+    caches = rotate_paged(case, copies)
+    b, hq, d = case.q.shape
+    hkv, bs = case.num_kv_heads, case.block_size
+    maxblk = case.block_table.shape[1]
+    s = lib.attn_decode_num_splits(b, hkv, bs, maxblk, splits)
+    ws = torch.zeros(max(1, lib.attn_decode_workspace_bytes(b, hkv, d, s)), dtype=torch.uint8, device=case.q.device)
+    out = torch.empty_like(case.q)
+    lse = torch.empty((b, hq), dtype=torch.float32, device=case.q.device)
+
+    def make(kc, vc):
+        return lambda: lib.attn_decode_paged(case.q, kc, vc, case.block_table, case.seq_lens_k, case.scale,
+                                             k_scale=case.k_scale, v_scale=case.v_scale, out=out, lse=lse,
+                                             num_splits=s, workspace=ws)
+    wall, durs = time_steps([make(kc, vc) for kc, vc in caches], steps, warmup)
+    kern = statistics.mean(durs)
+    log(f"[bench] {label}: splits={s} copies={copies} wall/step={wall:.4f} ms kernel mean={kern:.4f} "
+        f"median={statistics.median(durs):.4f} min={min(durs):.4f} ms -> {kv_bytes / kern / 1e6:.1f} GB/s")
+    return {"kv_bytes": kv_bytes, "splits": s, "wall_ms": wall, "kernel_ms_mean": kern,
+            "kernel_ms_median": statistics.median(durs), "kernel_ms_min": min(durs), "out": out, "lse": lse}
+
+
+def prefill_section(lib, case, steps, warmup):
+    from attention_gqa_flash_02_amd import workmodel
+    flops = workmodel.prefill_flops(case.seqlens, case.seqlens, case.num_q_heads, case.head_dim, case.causal)
+    out, lse = lib.attn_prefill_varlen(case.q, case.k, case.v, case.cu_seqlens, case.causal, case.scale,
+                                       max_seqlen=case.max_seqlen)
+
+    def call():
+        lib.attn_prefill_varlen(case.q, case.k, case.v, case.cu_seqlens, case.causal, case.scale, out=out,
+                                lse=lse, max_seqlen=case.max_seqlen)
+    wall, durs = time_steps([call], steps, warmup)
+    kern = statistics.mean(durs)
+    log(f"[bench] prefill: wall/step={wall:.4f} ms kernel mean={kern:.4f} min={min(durs):.4f} ms -> "
+        f"{flops / kern / 1e9:.1f} TFLOP/s")
+    return {"flops": flops, "wall_ms": wall, "kernel_ms_mean": kern, "kernel_ms_min": min(durs), "out": out,
+            "lse": lse}
+
+
+def sampled_parity_paged(case, out, lse, units):
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import oracle_paged, bf16_np
+    ref_o, ref_l = oracle_paged(case, units=units)
+    o = bf16_np(out)
+    m = ~np.isnan(ref_o)
+    err = np.abs(o[m] - ref_o[m])
+    l = lse.cpu().numpy().astype(np.float64)
+    lm = ~np.isnan(ref_l)
+    return {"units": len(units), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+            "lse_max_abs": float(np.abs(l[lm] - ref_l[lm]).max())}
+
+
+def sampled_parity_prefill(case, out, lse, units):
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import oracle_prefill, bf16_np
+    ref_o, ref_l = oracle_prefill(case, units=units)
+    o = bf16_np(out)
+    m = ~np.isnan(ref_o)
+    err = np.abs(o[m] - ref_o[m])
+    l = lse.cpu().numpy().astype(np.float64)
+    lm = ~np.isnan(ref_l)
+    return {"units": len(units), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+            "lse_max_abs": float(np.abs(l[lm] - ref_l[lm]).max())}
+
+
+def cpu_baseline_decode(case):
+    """The fp64 oracle over the whole decode workload on the host cores."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import bf16_np, cache_np
+    from oracle import parallel
+    from attention_gqa_flash_02_amd import workmodel
+    args = (bf16_np(case.q), cache_np(case.k_cache), cache_np(case.v_cache), case.block_table.cpu().numpy(),
+            case.cu_seqlens_q.cpu().numpy(), case.seq_lens_k.cpu().numpy(), True, case.scale)
+    b, hq, d = case.q.shape
+    units = [(i, h) for i in range(b) for h in range(hq)]
+    workers = min(16, os.cpu_count() or 1)
+    _, _, wall, used = parallel.run_units("paged", args, {"kv_format": "bf16"}, units,
+                                          case.cu_seqlens_q.cpu().numpy(), (b, hq, d), (b, hq), workers=workers)
+    kv = workmodel.kv_bytes(case.kv_lens, case.num_kv_heads, case.head_dim, 2)
+    return {"value": kv / wall / 1e9, "unit": "GB/s", "cores": used, "kind": "oracle",
+            "sample": f"the whole decode batch ({b} requests x {hq} heads, {kv / 1e6:.0f} MB of KV), "
+                      f"fp64 numpy, one BLAS thread per worker process; wall {wall:.2f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); this library has no multi-GPU "
+              f"path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import attention_gqa_flash_02_amd as lib
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] device: {torch.cuda.get_device_name(dev)}; library {lib.library_path()}")
+
+    # ---- headline: paged GQA decode, batch 32 (generated on the host, copied to the GPU)
+    t = time.perf_counter()
+    c2 = synth.config_case("c2")
+    c2_host = c2
+    c2 = synth.PagedCase(**{k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in vars(c2).items()})
+    log(f"[bench] decode workload ready in {time.perf_counter() - t:.1f} s: sum(len)={sum(c2.kv_lens)}")
+    dec = decode_section(lib, c2, a.splits, a.steps, a.warmup, "decode c2")
+    result_extra = {}
+    if not a.quick:
+        rng = np.random.default_rng(0)
+        units = [(int(b), int(h)) for b, h in zip(rng.integers(0, 32, 64), rng.integers(0, 32, 64))]
+        par = sampled_parity_paged(c2_host, dec["out"], dec["lse"], units)
+        log(f"[bench] decode c2 parity on {par['units']} sampled (request, head) units: {par}")
+        result_extra["decode_parity_sample"] = par
+
+    if not a.no_extra:
+        # ---- causal varlen prefill 4 x 8192 (generated on the GPU)
+        c3 = synth.config_case("c3", device=dev)
+        pre = prefill_section(lib, c3, max(5, a.steps // 5), max(2, a.warmup // 2))
+        tf = pre["flops"] / pre["kernel_ms_mean"] / 1e9
+        result_extra["prefill_c3"] = {
+            "workload": "causal varlen prefill, 4 x 8192 tokens, 32/8 heads, D 128, bf16, out + LSE",
+            "tflops": tf, "ms": pre["kernel_ms_mean"], "wall_ms": pre["wall_ms"],
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": tf / MFMA_BF16_PEAK_TFS, "traffic": None},
+            "algorithmic_flops": pre["flops"]}
+        if not a.quick:
+            units = [(0, 0), (1, 7), (2, 19), (3, 31)]
+            par = sampled_parity_prefill(c3, pre["out"], pre["lse"], units)
+            log(f"[bench] prefill parity on {units}: {par}")
+            result_extra["prefill_c3"]["parity_sample"] = par
+        del c3, pre
+        torch.cuda.empty_cache()
+
+        # ---- long-context split-KV decode 2 x 131072 (generated on the GPU)
+        c4 = synth.config_case("c4", device=dev)
+        best = None
+        for s in (16, 32, 64, 128, 256):
+            r = decode_section(lib, c4, s, a.steps, a.warmup, f"decode c4 splits={s}")
+            if best is None or r["kernel_ms_mean"] < best["kernel_ms_mean"]:
+                best = r
+        gbs = best["kv_bytes"] / best["kernel_ms_mean"] / 1e6
+        result_extra["decode_c4"] = {
+            "workload": "split-KV decode, 2 x 131072 tokens, 32/2 heads, D 128, bf16 KV, 64-token blocks",
+            "gbs": gbs, "splits": best["splits"], "ms": best["kernel_ms_mean"],
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+        del c4
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline_decode(c2_host)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    achieved = dec["kv_bytes"] / dec["kernel_ms_mean"] / 1e6
+    value = dec["kv_bytes"] / dec["wall_ms"] / 1e6
+    line = {
+        "metric": "decode attn KV GB/s (% HBM peak)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(dec["wall_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled pages)",
+        "config": {"workload": "paged GQA decode: batch 32, 32 q / 8 kv heads, head_dim 128, bf16 KV in "
+                               "16-token blocks, lengths U[1024, 8192]",
+                   "global_batch": 32, "seq_len": "U[1024, 8192]", "num_splits": dec["splits"],
+                   "kv_bytes": dec["kv_bytes"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "extra": result_extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

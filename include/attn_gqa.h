@@ -93,8 +93,8 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v,
 /*
  * Number of KV partitions a paged decode call will use (split-KV, "Attention
  * kernels", section "Prefill and decode attention"). requested > 0 is
- * returned unchanged (clamped to the number of 16-token tiles of the longest
- * request); requested == 0 picks one from the batch shape and the device's
+ * returned clamped to the number of 64-key chunks of the longest possible
+ * request (max_blocks_per_seq * block_size keys) and to 4096; requested == 0 picks one from the batch shape and the device's
  * compute-unit count. Returns 0 on invalid sizes.
  */
 int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
@@ -103,8 +103,11 @@ int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t b
 /*
  * Workspace bytes a paged decode / varlen-paged call needs for num_splits
  * (resolved, >= 1) partitions: per (request, kv head, partition) a block of
- * 16 rows x head_dim fp32 partial outputs plus 16 fp32 partial LSEs.
- * 0 when num_splits == 1 (no partials are written).
+ * 16 rows x head_dim fp32 partial outputs plus 16 fp32 partial LSEs, and one
+ * 32-bit completion counter per (request, kv head). 0 when num_splits == 1.
+ * The counters must be zero when a workspace is first used (zero-fill it once
+ * after allocating it); every completed call leaves them at zero again.
+ * Calls that share one workspace must not overlap in time.
  */
 size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t num_splits);
@@ -114,7 +117,7 @@ size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32
  * Each KV head is read once for all num_q_heads / num_kv_heads query heads of
  * its group ("Attention kernels", section "Prefill and decode attention"); the
  * key axis is cut into num_splits partitions of
- *   C = roundup(ceil(max_blocks_per_seq * block_size / num_splits), 16) tokens,
+ *   C = roundup(ceil(max_blocks_per_seq * block_size / num_splits), 64) tokens,
  * partition s covering keys [s*C, min((s+1)*C, seq_lens[b])), and the
  * partitions are merged with their log-sum-exps.
  *   q [num_seqs, num_q_heads, head_dim] bf16 (the newest token of each request)
@@ -125,7 +128,9 @@ size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32
  *   out [num_seqs, num_q_heads, head_dim] bf16; lse [num_seqs, num_q_heads] fp32 or NULL
  *   num_splits: 0 = automatic (attn_decode_num_splits), else the partition count
  *   workspace: device scratch of >= attn_decode_workspace_bytes(...) bytes
- *   (may be NULL when that is 0); its contents on entry do not matter.
+ *   (may be NULL when that is 0), zero-filled before its first use (see above).
+ *   Partitions are merged inside the same launch by the last partition of each
+ *   (request, kv head) to finish.
  * Requires num_q_heads / num_kv_heads <= 16.
  */
 attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,

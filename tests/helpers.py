@@ -52,7 +52,8 @@ def compare(out, lse, ref_out, ref_lse, max_abs=MAX_ABS, mean_abs=MEAN_ABS, lse_
         l = lse.detach().cpu().numpy().astype(np.float64)
         lm = ~np.isnan(ref_lse)
         both_inf = np.isneginf(l[lm]) & np.isneginf(ref_lse[lm])
-        lerr = np.where(both_inf, 0.0, np.abs(l[lm] - ref_lse[lm]))
+        with np.errstate(invalid="ignore"):
+            lerr = np.where(both_inf, 0.0, np.abs(l[lm] - ref_lse[lm]))
         stats["lse_max_abs"] = float(lerr.max()) if lerr.size else 0.0
     print(f"[parity] {label} {stats}", flush=True)
     assert np.isfinite(o[mask]).all(), f"{label}: non-finite outputs"
