@@ -120,8 +120,7 @@ def _workspace(nbytes, device, workspace):
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace too small: need {nbytes} bytes")
         return workspace
-    # zero-filled: the completion counters at its end must start at zero
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale=None, v_scale=None,

@@ -116,8 +116,7 @@ int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t b
 size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t num_splits) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_splits <= 1) return 0;
-  return (size_t)num_seqs * num_kv_heads * num_splits * 16 * ((size_t)head_dim + 1) * sizeof(float) +
-         (size_t)num_seqs * num_kv_heads * sizeof(unsigned);
+  return (size_t)num_seqs * num_kv_heads * num_splits * 16 * ((size_t)head_dim + 1) * sizeof(float);
 }
 
 static attn_status validate_paged(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
@@ -170,7 +169,6 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   const size_t ws_o_elems = (size_t)num_seqs * num_kv_heads * S * 16 * head_dim;
   p.ws_o = need ? static_cast<float*>(workspace) : nullptr;
   p.ws_lse = need ? static_cast<float*>(workspace) + ws_o_elems : nullptr;
-  p.counters = need ? reinterpret_cast<unsigned*>(p.ws_lse + (size_t)num_seqs * num_kv_heads * S * 16) : nullptr;
   p.scale = scale;
   p.num_seqs = num_seqs;
   p.Hq = num_q_heads;

@@ -12,9 +12,9 @@ namespace attn {
 // walked heaviest (last) first.
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, hipStream_t stream);
 
-// Split-KV paged decode, one launch (grid: partitions x kv heads x requests); the last partition
-// of each (request, kv head) to finish merges the partitions. rows_max = rows per
-// (request, kv head) sizing the LDS combine buffer (<= 16).
+// Split-KV paged decode (grid: partitions x kv heads x requests), followed, when there is more
+// than one partition, by the LSE merge (grid: rows x kv heads x requests). rows_max = rows per
+// (request, kv head) (<= 16); it sizes the LDS combine buffer and the merge grid.
 hipError_t launch_decode(const PagedParams& p, int head_dim, int kv_type, int rows_max, hipStream_t stream);
 
 // Number of CUs of the current device (cached per device).

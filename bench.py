@@ -88,7 +88,7 @@ def decode_section(lib, case, splits, steps, warmup, label):
     hkv, bs = case.num_kv_heads, case.block_size
     maxblk = case.block_table.shape[1]
     s = lib.attn_decode_num_splits(b, hkv, bs, maxblk, splits)
-    ws = torch.zeros(max(1, lib.attn_decode_workspace_bytes(b, hkv, d, s)), dtype=torch.uint8, device=case.q.device)
+    ws = torch.empty(max(1, lib.attn_decode_workspace_bytes(b, hkv, d, s)), dtype=torch.uint8, device=case.q.device)
     out = torch.empty_like(case.q)
     lse = torch.empty((b, hq), dtype=torch.float32, device=case.q.device)
 

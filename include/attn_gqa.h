@@ -94,8 +94,8 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v,
  * Number of KV partitions a paged decode call will use (split-KV, "Attention
  * kernels", section "Prefill and decode attention"). requested > 0 is
  * returned clamped to the number of 64-key chunks of the longest possible
- * request (max_blocks_per_seq * block_size keys) and to 4096; requested == 0 picks one from the batch shape and the device's
- * compute-unit count. Returns 0 on invalid sizes.
+ * request (max_blocks_per_seq * block_size keys) and to 4096; requested == 0
+ * picks one from the batch shape and the device's compute-unit count. Returns 0 on invalid sizes.
  */
 int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                                int32_t max_blocks_per_seq, int32_t requested);
@@ -103,11 +103,9 @@ int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t b
 /*
  * Workspace bytes a paged decode / varlen-paged call needs for num_splits
  * (resolved, >= 1) partitions: per (request, kv head, partition) a block of
- * 16 rows x head_dim fp32 partial outputs plus 16 fp32 partial LSEs, and one
- * 32-bit completion counter per (request, kv head). 0 when num_splits == 1.
- * The counters must be zero when a workspace is first used (zero-fill it once
- * after allocating it); every completed call leaves them at zero again.
- * Calls that share one workspace must not overlap in time.
+ * 16 rows x head_dim fp32 partial outputs plus 16 fp32 partial LSEs. 0 when
+ * num_splits == 1. The contents need no initialisation; calls that share one
+ * workspace must not overlap in time (enqueue them on one stream).
  */
 size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t num_splits);
@@ -128,9 +126,10 @@ size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32
  *   out [num_seqs, num_q_heads, head_dim] bf16; lse [num_seqs, num_q_heads] fp32 or NULL
  *   num_splits: 0 = automatic (attn_decode_num_splits), else the partition count
  *   workspace: device scratch of >= attn_decode_workspace_bytes(...) bytes
- *   (may be NULL when that is 0), zero-filled before its first use (see above).
- *   Partitions are merged inside the same launch by the last partition of each
- *   (request, kv head) to finish.
+ *   (may be NULL when that is 0).
+ * A request whose keys fit one partition is written directly; otherwise every
+ * partition writes a normalised partial output and its LSE to the workspace,
+ * and a second kernel, enqueued on the same stream, merges them.
  * Requires num_q_heads / num_kv_heads <= 16.
  */
 attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,

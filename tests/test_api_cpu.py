@@ -85,7 +85,7 @@ def test_split_planning_and_workspace_sizes():
     assert lib.attn_decode_num_splits(1, 1, 16, 1, 8) == 1
     assert lib.attn_decode_num_splits(0, 1, 16, 1, 8) == 0
     assert lib.attn_decode_workspace_bytes(2, 2, 128, 1) == 0
-    assert lib.attn_decode_workspace_bytes(2, 2, 128, 64) == 2 * 2 * 64 * 16 * 129 * 4 + 2 * 2 * 4
+    assert lib.attn_decode_workspace_bytes(2, 2, 128, 64) == 2 * 2 * 64 * 16 * 129 * 4
 
 
 def test_varlen_validation():
