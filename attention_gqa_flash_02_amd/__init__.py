@@ -100,9 +100,10 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, causal, scale, out=None, lse=None, 
     return out, lse
 
 
-def attn_decode_num_splits(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, requested=0):
-    return int(_lib.load().attn_decode_num_splits(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
-                                                  requested))
+def attn_decode_num_splits(num_seqs, num_kv_heads, head_dim, kv_dtype, block_size, max_blocks_per_seq,
+                           requested=0):
+    return int(_lib.load().attn_decode_num_splits(num_seqs, num_kv_heads, head_dim, kv_dtype, block_size,
+                                                  max_blocks_per_seq, requested))
 
 
 def attn_decode_workspace_bytes(num_seqs, num_kv_heads, head_dim, num_splits):
@@ -143,7 +144,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale
     b, hq, d = q.shape
     nblk, hkv, bs, _ = k_cache.shape
     maxblk = block_table.shape[1]
-    splits = attn_decode_num_splits(b, hkv, bs, maxblk, num_splits)
+    splits = attn_decode_num_splits(b, hkv, d, kvt, bs, maxblk, num_splits)
     ws = _workspace(attn_decode_workspace_bytes(b, hkv, d, splits), dev, workspace)
     if out is None:
         out = torch.empty_like(q)
@@ -180,7 +181,7 @@ def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k
     if max_q_len is None:
         cu = cu_seqlens_q.cpu()
         max_q_len = int((cu[1:] - cu[:-1]).max()) if cu.numel() > 1 else 0
-    splits = attn_decode_num_splits(b, hkv, bs, maxblk, num_splits)
+    splits = attn_decode_num_splits(b, hkv, d, kvt, bs, maxblk, num_splits)
     ws = _workspace(attn_varlen_workspace_bytes(b, hkv, d, splits), dev, workspace)
     if out is None:
         out = torch.empty_like(q)

@@ -12,11 +12,17 @@ namespace attn {
 int device_cu_count() {
   static std::atomic<int> cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
   int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
   cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
@@ -34,12 +40,12 @@ static int gcd_int(int a, int b) {
   return a;
 }
 
-// Partition length for a given count: a multiple of 64 keys (one wave chunk).
-static int split_tokens_for(int max_len, int num_splits) {
-  int per = (max_len + num_splits - 1) / num_splits;
-  per = ((per + 63) / 64) * 64;
-  return per > 0 ? per : 64;
-}
+// Upper bound on decode partitions: the merge kernel keeps one weight per partition in LDS.
+constexpr int kMaxSplits = 4096;
+// Upper bound on requests of a paged call: the partition kernel keeps one chunk offset per
+// request in LDS.
+constexpr int kMaxPagedSeqs = 16384;
+
 
 }  // namespace attn
 
@@ -90,33 +96,27 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v, con
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
-                               int32_t max_blocks_per_seq, int32_t requested) {
-  if (num_seqs <= 0 || num_kv_heads <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || requested < 0)
+int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t kv_dtype,
+                               int32_t block_size, int32_t max_blocks_per_seq, int32_t requested) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || requested < 0 ||
+      (head_dim != 128 && head_dim != 256) || (kv_dtype != ATTN_KV_BF16 && kv_dtype != ATTN_KV_FP8_E4M3FN))
     return 0;
+  const int kvt = kv_dtype == ATTN_KV_BF16 ? KV_BF16 : KV_FP8;
+  const long long ch = decode_chunk_tokens(head_dim, kvt);
   const long long max_len = (long long)max_blocks_per_seq * block_size;
-  const int max_chunks = (int)((max_len + 63) / 64);
-  int s;
-  if (requested > 0) {
-    s = requested;
-  } else {
-    // Aim for about four partition workgroups per compute unit, each at least 256 keys long.
-    const long long units = (long long)num_seqs * num_kv_heads;
-    const long long target = 4LL * device_cu_count();
-    long long want = (target + units - 1) / units;
-    const long long cap = (max_len + 255) / 256;
-    if (want > cap) want = cap;
-    s = (int)(want < 1 ? 1 : want);
-  }
-  if (s > max_chunks) s = max_chunks;
-  if (s > 4096) s = 4096;
-  return s < 1 ? 1 : s;
+  // useful shares: at most one per 4 chunks of the largest possible batch
+  const long long max_shares = ((long long)num_seqs * num_kv_heads * ((max_len + ch - 1) / ch) + 3) / 4;
+  long long s = requested > 0 ? requested : (long long)decode_wgs_per_cu(head_dim, kvt) * device_cu_count();
+  if (s > max_shares) s = max_shares;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return (int32_t)(s < 1 ? 1 : s);
 }
 
 size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t num_splits) {
-  if (num_seqs <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_splits <= 1) return 0;
-  return (size_t)num_seqs * num_kv_heads * num_splits * 16 * ((size_t)head_dim + 1) * sizeof(float);
+  if (num_seqs <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
+  return (size_t)num_splits * 2 * 16 * ((size_t)head_dim + 1) * sizeof(float) +
+         ((size_t)num_seqs + 1) * sizeof(int32_t);
 }
 
 static attn_status validate_paged(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
@@ -133,6 +133,7 @@ static attn_status validate_paged(const void* q, const void* k_cache, const void
     return ATTN_ERR_SHAPE;
   if (head_dim != 128 && head_dim != 256) return ATTN_ERR_UNSUPPORTED;
   if (!supported_block_size(block_size)) return ATTN_ERR_UNSUPPORTED;
+  if (num_seqs > kMaxPagedSeqs) return ATTN_ERR_UNSUPPORTED;
   if ((long long)max_blocks_per_seq * block_size > INT_MAX / 2) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
@@ -151,9 +152,10 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
   const int g = num_q_heads / num_kv_heads;
   if (g > 16) return ATTN_ERR_UNSUPPORTED;
-  const int S = attn_decode_num_splits(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, num_splits);
+  const int S = attn_decode_num_splits(num_seqs, num_kv_heads, head_dim, kv_dtype, block_size,
+                                       max_blocks_per_seq, num_splits);
   const size_t need = attn_decode_workspace_bytes(num_seqs, num_kv_heads, head_dim, S);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
 
   PagedParams p{};
   p.q = static_cast<const bf16*>(q);
@@ -166,9 +168,9 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   p.cu_seqlens_q = nullptr;
   p.out = static_cast<bf16*>(out);
   p.lse = lse;
-  const size_t ws_o_elems = (size_t)num_seqs * num_kv_heads * S * 16 * head_dim;
-  p.ws_o = need ? static_cast<float*>(workspace) : nullptr;
-  p.ws_lse = need ? static_cast<float*>(workspace) + ws_o_elems : nullptr;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_lse = p.ws_o + (size_t)S * 2 * 16 * head_dim;
+  p.ws_prefix = reinterpret_cast<int32_t*>(p.ws_lse + (size_t)S * 2 * 16);
   p.scale = scale;
   p.num_seqs = num_seqs;
   p.Hq = num_q_heads;
@@ -176,8 +178,7 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   p.g = g;
   p.bs = block_size;
   p.max_blocks = max_blocks_per_seq;
-  p.num_splits = S;
-  p.split_tokens = split_tokens_for(max_blocks_per_seq * block_size, S);
+  p.num_wg = S;
   p.causal = 1;
   hipError_t e = launch_decode(p, head_dim, kv_dtype == ATTN_KV_BF16 ? KV_BF16 : KV_FP8, g,
                                static_cast<hipStream_t>(stream));

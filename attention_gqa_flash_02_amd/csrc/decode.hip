@@ -4,39 +4,45 @@
 namespace attn {
 
 template <int D, int KVT, int NU>
-__global__ __launch_bounds__(256) void decode_split_kernel(PagedParams p) {
+__global__ __launch_bounds__(256) void decode_share_kernel(PagedParams p, int combine_floats) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  decode_unit<D, KVT, NU>(p, blockIdx.z, blockIdx.y, blockIdx.x, reinterpret_cast<float*>(smem_raw));
+  decode_share<D, KVT, NU>(p, reinterpret_cast<float*>(smem_raw), combine_floats);
 }
 
-template <int D>
+template <int D, int CH>
 __global__ __launch_bounds__(256) void decode_merge_kernel(PagedParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  merge_row<D>(p, blockIdx.z, blockIdx.y, blockIdx.x, reinterpret_cast<float*>(smem_raw));
-}
-
-// Partition kernel LDS: 128 floats of statistics plus four waves' O rows.
-static size_t decode_lds_bytes(int rows_max, int head_dim) {
-  return (128 + 4 * (size_t)rows_max * head_dim) * sizeof(float);
+  merge_row<D, CH>(p, blockIdx.z, blockIdx.y, blockIdx.x, reinterpret_cast<float*>(smem_raw));
 }
 
 template <int D, int KVT, int NU>
 static hipError_t launch_decode_t(const PagedParams& p, int rows_max, hipStream_t stream) {
-  static bool attr_set = false;  // per process; the attribute is a property of the function
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_split_kernel<D, KVT, NU>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)decode_lds_bytes(16, D));
+  // partition kernel LDS: 128 floats of statistics, four waves' O rows, then the chunk prefix
+  // sums and 4 scratch ints
+  const int combine_floats = 128 + 4 * rows_max * D;
+  const size_t lds = (size_t)combine_floats * sizeof(float) + ((size_t)p.num_seqs + 5) * sizeof(int);
+  // the dynamic-LDS limit of each kernel is raised to the largest size launched so far
+  static size_t lds_set = 0;
+  if (lds > lds_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_share_kernel<D, KVT, NU>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    lds_set = lds;
   }
-  dim3 grid(p.num_splits, p.Hkv, p.num_seqs);
-  hipLaunchKernelGGL((decode_split_kernel<D, KVT, NU>), grid, dim3(256), decode_lds_bytes(rows_max, D), stream, p);
+  hipLaunchKernelGGL((decode_share_kernel<D, KVT, NU>), dim3(p.num_wg), dim3(256), lds, stream, p, combine_floats);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.num_splits <= 1) return e;
-  const size_t merge_lds = ((size_t)p.num_splits + (256 / (D / 4)) * D) * sizeof(float);
+  if (e != hipSuccess) return e;
+  constexpr int CH = DecodeShape<NU>::CH;
+  const size_t merge_lds = ((size_t)p.num_wg + (256 / (D / 4)) * D) * sizeof(float);
+  static size_t merge_lds_set = 0;
+  if (merge_lds > merge_lds_set) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_merge_kernel<D, CH>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)merge_lds);
+    if (e != hipSuccess) return e;
+    merge_lds_set = merge_lds;
+  }
   dim3 mgrid(rows_max, p.Hkv, p.num_seqs);
-  hipLaunchKernelGGL((decode_merge_kernel<D>), mgrid, dim3(256), merge_lds, stream, p);
+  hipLaunchKernelGGL((decode_merge_kernel<D, CH>), mgrid, dim3(256), merge_lds, stream, p);
   return hipGetLastError();
 }
 
@@ -46,6 +52,35 @@ hipError_t launch_decode(const PagedParams& p, int head_dim, int kv_type, int ro
   if (head_dim == 128 && kv_type == KV_FP8) return launch_decode_t<128, KV_FP8, 4>(p, rows_max, stream);
   if (head_dim == 256 && kv_type == KV_FP8) return launch_decode_t<256, KV_FP8, 2>(p, rows_max, stream);
   return hipErrorInvalidValue;
+}
+
+int decode_chunk_tokens(int head_dim, int kv_type) {
+  (void)kv_type;
+  return head_dim == 128 ? DecodeShape<4>::CH : DecodeShape<2>::CH;
+}
+
+template <int D, int KVT, int NU>
+static int wgs_per_cu_t() {
+  // Resident partition workgroups per compute unit (the register-limited occupancy of the
+  // variant), queried once; a failed query leaves no pending error and counts as 1.
+  static int cached = 0;
+  if (cached > 0) return cached;
+  int n = 0;
+  const void* fn = reinterpret_cast<const void*>(&decode_share_kernel<D, KVT, NU>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, 16 * 1024) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 1;
+  }
+  cached = n;
+  return n;
+}
+
+int decode_wgs_per_cu(int head_dim, int kv_type) {
+  if (head_dim == 128 && kv_type == KV_BF16) return wgs_per_cu_t<128, KV_BF16, 4>();
+  if (head_dim == 256 && kv_type == KV_BF16) return wgs_per_cu_t<256, KV_BF16, 2>();
+  if (head_dim == 128 && kv_type == KV_FP8) return wgs_per_cu_t<128, KV_FP8, 4>();
+  if (head_dim == 256 && kv_type == KV_FP8) return wgs_per_cu_t<256, KV_FP8, 2>();
+  return 1;
 }
 
 }  // namespace attn

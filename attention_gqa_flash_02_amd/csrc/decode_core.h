@@ -1,36 +1,45 @@
-// Split-KV paged decode for gfx950: one workgroup = (request, kv head, KV partition).
+// Split-KV paged decode for gfx950.
 //
 // What it computes ("Attention kernels", section "Prefill and decode attention"):
 // the few query rows of a request that share one KV head (g query heads x Lq
 // new tokens, at most 16 rows) attend over the request's paged cache; each KV
-// head is read once for all of them, and the key axis is cut into partitions
-// whose results are merged with their log-sum-exps (the same rule as the
-// online softmax). Pages are located through the block table ("Optimization
-// 1", section 3.4; "Attention kernels", section "Paged KV and kernels").
+// head is read once for all of them, and the key axis is cut into pieces whose
+// results are merged with their log-sum-exps (the same rule as the online
+// softmax). Pages are located through the block table ("Optimization 1",
+// section 3.4; "Attention kernels", section "Paged KV and kernels").
+//
+// Work split: the batch's work is the list of (request, kv head, chunk of CH
+// keys) items, request-major. The partition kernel's G workgroups take equal
+// contiguous shares of that list (a multiple of 4 chunks each), so every
+// workgroup streams the same number of KV bytes whatever the mix of context
+// lengths. A share covers pieces of one or more (request, kv head) units; a
+// unit that lies inside one share is written directly, the pieces of a unit
+// that spans shares go to the workspace as normalised partials with their LSEs
+// and are merged by a second small kernel.
 //
 // Work layout inside a workgroup (4 waves):
-//   * the partition is walked in chunks of CH = 16*NU tokens; wave w takes
-//     chunks w, w+4, ...
+//   * the share's chunks are dealt to the waves round-robin.
 //   * per chunk, S^T = K . Q^T on 16x16x32 MFMA (NU sub-tiles of 16 keys; the
 //     16 query rows are the MFMA columns), an online-softmax update in
-//     registers, then O^T += V^T . P^T on 16x16x16 MFMA. V pages are stored
+//     registers, then O^T += V^T . P^T on 16x16x32 MFMA. V pages are stored
 //     token-innermost ([D][block_size]), so the V^T operand comes straight from
 //     HBM with the key axis contiguous in each lane; P^T is the S^T accumulator
 //     itself (no shuffle, no LDS).
-//   * the key held by A-row i of sub-tile u is chunk token RUN*(i/4) + 4*u + i%4
-//     (RUN = 4*NU), so that C-row 4*q + s of sub-tile u is token RUN*q + 4*u + s:
-//     each lane quad then owns one contiguous RUN-token run, which is what its
-//     V^T loads need, and a run never crosses a page (block sizes are >= 16).
+//   * token layout: in half h (32 tokens) of a chunk, lane quad q owns the
+//     8-token run 32h + 8q .. +7. A-row i of QK sub-tile u = 2h + e loads token
+//     32h + 8(i/4) + 4e + i%4, so that C-row 4q + s of that sub-tile is token
+//     32h + 8q + 4e + s: each lane then holds P for exactly the 8 tokens its own
+//     V^T load brings (one 16-byte load per d row for bf16), and a run never
+//     crosses a page (block sizes are >= 16).
 //   * memory: the block-table entries of the next chunk are loaded while the
 //     current chunk computes, and the K and V loads of a chunk are issued back
 //     to back with no wait in between. Loads past the end of the request are
 //     redirected into its last page (always a valid address) and their values
 //     masked, so no load sits behind a branch.
-//   * the four waves' (max, sum, O) are combined in LDS in a fixed order. A
-//     request that needs one partition writes out/lse directly; otherwise each
-//     partition writes a normalised partial and its LSE, and a second small
-//     kernel merges them.
+//   * the four waves' (max, sum, O) are combined in LDS in a fixed order.
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -49,23 +58,52 @@ struct PagedParams {
   const int32_t* cu_seqlens_q; // [B + 1], or nullptr: request b owns q row b
   bf16* out;                   // [Tq, Hq, D]
   float* lse;                  // [Tq, Hq] or nullptr
-  float* ws_o;                 // [B, Hkv, S, 16, D] partial outputs (normalised)
-  float* ws_lse;               // [B, Hkv, S, 16] partial natural-log LSEs
+  float* ws_o;                 // [G, 2, 16, D] partial outputs (normalised)
+  float* ws_lse;               // [G, 2, 16] partial natural-log LSEs
+  int32_t* ws_prefix;          // [B + 1] chunk-count prefix sums, written by workgroup 0
   float scale;
-  int num_seqs, Hq, Hkv, g, bs, max_blocks, num_splits, split_tokens, causal;
+  int num_seqs, Hq, Hkv, g, bs, max_blocks, num_wg, causal;
 };
+
+// Chunk count of request b on this path (0 when its rows belong to another path or it has
+// no new rows): ceil(len / CH) chunks per kv head.
+template <int CH>
+__device__ __forceinline__ int decode_chunks(const PagedParams& p, int b) {
+  const int len = p.seq_lens_k[b];
+  int rows = p.g;
+  if (p.cu_seqlens_q) rows = (p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b]) * p.g;
+  return (rows > 0 && rows <= 16) ? (len + CH - 1) / CH : 0;
+}
+
+// First chunk of workgroup g's share of T chunks: shares are whole groups of 4 chunks,
+// as equal as possible.
+__device__ __forceinline__ long long share_start(long long g, long long T, int G) {
+  const long long quads = (T + 3) / 4;
+  const long long s = 4 * ((g * quads) / G);
+  return s < T ? s : T;
+}
+// The workgroup whose share holds chunk x (0 <= x < T).
+__device__ __forceinline__ int share_of(long long x, long long T, int G) {
+  const long long quads = (T + 3) / 4;
+  return (int)(((x / 4 + 1) * G + quads - 1) / quads - 1);
+}
 
 template <int NU>
 struct DecodeShape {
+  static_assert(NU == 2 || NU == 4, "a chunk is one or two 32-token halves");
   static constexpr int CH = 16 * NU;   // tokens per wave iteration
-  static constexpr int RUN = 4 * NU;   // consecutive tokens owned by one lane quad
+  static constexpr int NH = NU / 2;    // 32-token halves per chunk
 };
 
-// Rows of a request on this path: r -> (new token r / g, query head kvh*g + r % g).
+// One piece of a (request, kv head) unit: chunks [c0, c1) of the unit; the waves start at chunk
+// c0 + first[w] and step by 4 chunks. Rows of a request on this path: r -> (new token r / g,
+// query head kvh*g + r % g). slot < 0: the piece is the whole unit and is written to out/lse;
+// else it is written to partial slot `slot` of the workspace.
 template <int D, int KVT, int NU>
-__device__ __forceinline__ void decode_unit(const PagedParams& p, int b, int kvh, int split, float* lds) {
+__device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kvh, int c0, int c1, int wave_first,
+                                             int slot, float* lds) {
   constexpr int CH = DecodeShape<NU>::CH;
-  constexpr int RUN = DecodeShape<NU>::RUN;
+  constexpr int NH = DecodeShape<NU>::NH;
   constexpr int KK = D / 32;        // QK MFMAs per 16-key sub-tile
   constexpr int NB = D / 16;        // 16-wide d blocks of O^T
   constexpr int ELT = (KVT == KV_BF16) ? 2 : 1;
@@ -79,16 +117,13 @@ __device__ __forceinline__ void decode_unit(const PagedParams& p, int b, int kvh
   const int q0 = p.cu_seqlens_q ? p.cu_seqlens_q[b] : b;
   const int qlen = p.cu_seqlens_q ? (p.cu_seqlens_q[b + 1] - q0) : 1;
   const int R = qlen * p.g;
-  const int C = p.split_tokens;
-  const int n_splits_b = (len + C - 1) / C;          // non-empty partitions of this request
-  if (split >= (n_splits_b > 0 ? n_splits_b : 1)) return;
-  const bool direct = (n_splits_b <= 1);              // write out/lse here, no merge needed
-  const int t_begin = split * C;
-  const int t_end = min(len, t_begin + C);
+  const bool direct = slot < 0;
+  const int t_end = min(len, c1 * CH);
 
   float kscale = 1.f, vscale = 1.f;
   if (KVT == KV_FP8) { kscale = p.k_scale[kvh]; vscale = p.v_scale[kvh]; }
   const float c = p.scale * kscale * kLog2e;           // base-2 exponent per raw score unit
+  constexpr float kLazyRescale = 8.f;                  // see the running statistics below
 
   // ---- Q^T operands (B of the QK MFMA): lane (j = row, qd) holds Q[row][d-slots].
   bf16x8 qB[KK];
@@ -113,80 +148,92 @@ __device__ __forceinline__ void decode_unit(const PagedParams& p, int b, int kvh
     }
   }
 
-  float m = kNegInf;        // running max of raw scores of row j (same in all 4 quads)
-  float l = 0.f;            // this lane's share of the running exp-sum
-  f32x4 acc[NB];            // O^T[16n + 4qd + s][row j]
+  // Running statistics of row j, in the base-2 exponent domain t = c * s: mc is a reference
+  // maximum (the same in all four quads), l this lane's share of sum 2^(t - mc). The reference
+  // is only moved when a row's maximum exceeds it by more than kLazyRescale (so P <= 2^8 and
+  // the O rescale is skipped on almost every chunk); any reference gives the same result.
+  float mc = kNegInf;
+  float l = 0.f;
+  f32x4 acc[NB];            // O^T[16n + 4qd + r][row j], scaled by 2^-mc
 #pragma unroll
   for (int n = 0; n < NB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const size_t page_elems = (size_t)p.bs * D;         // elements per (block, kv head) page
+  const size_t page_bytes = (size_t)p.bs * D * ELT;   // bytes per (block, kv head) page
   const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
-  const char* kc = reinterpret_cast<const char*>(p.k_cache);
-  const char* vc = reinterpret_cast<const char*>(p.v_cache);
+  const char* kc = reinterpret_cast<const char*>(p.k_cache) + (size_t)kvh * page_bytes;
+  const char* vc = reinterpret_cast<const char*>(p.v_cache) + (size_t)kvh * page_bytes;
+  const size_t block_stride = (size_t)p.Hkv * page_bytes;
   const int last_tok = len - 1;
+  const int min_limit = p.causal ? (len - qlen) : (len - 1);   // smallest last-visible key of any row
 
-  // Block-table entries of a chunk: lane (j, qd) reads keys from the run at RUN*(j/4) (K) and
-  // the run at RUN*qd (V). Runs past the end of the request read its last page instead.
-  auto k_block = [&](int T0) { return min(T0 + RUN * (j >> 2), last_tok) / p.bs; };
-  auto v_block = [&](int T0) { return min(T0 + RUN * qd, last_tok) / p.bs; };
+  // Token layout of a chunk: in half h (32 tokens), lane quad q owns the 8-token run
+  // T0 + 32h + 8q .. +7, and score slot s of sub-tile u = 2h + e is token T0 + 32h + 8q + 4e + s.
+  // A K lane j loads the run of quad j/4, a V lane the run of its own quad. Runs past the end of
+  // the request read its last page instead (and are masked). Within a page the run starts at
+  // slot (T0 + 32h) % bs + 8q % bs (T0 is a multiple of 64 and bs of 16).
+  const int kq8 = (8 * (j >> 2)) % p.bs;
+  const int vq8 = (8 * qd) % p.bs;
+  auto k_block = [&](int T0, int h) { return min(T0 + 32 * h + 8 * (j >> 2), last_tok) / p.bs; };
+  auto v_block = [&](int T0, int h) { return min(T0 + 32 * h + 8 * qd, last_tok) / p.bs; };
 
-  int T0 = t_begin + CH * wave;
-  int kphys = 0, vphys = 0;
+  int T0 = (c0 + wave_first) * CH;
+  int kphys[NH], vphys[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) kphys[h] = vphys[h] = 0;
   if (T0 < t_end) {
-    kphys = table[k_block(T0)];
-    vphys = table[v_block(T0)];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      kphys[h] = table[k_block(T0, h)];
+      vphys[h] = table[v_block(T0, h)];
+    }
   }
 
+  constexpr int KW = (KVT == KV_BF16) ? KK : KK / 2;    // 16-byte K loads per key row
+  typedef typename std::conditional<KVT == KV_BF16, u32x4, u32x2>::type vword;
   for (; T0 < t_end; T0 += 4 * CH) {
     // ---------------- issue the K and V loads of this chunk
-    const int kt = T0 + RUN * (j >> 2);                 // first token of the lane's K run
-    const int kslot = kt % p.bs;                        // the run never crosses a page
-    const char* kpage = kc + ((size_t)kphys * p.Hkv + kvh) * page_elems * ELT;
-    constexpr int KW = (KVT == KV_BF16) ? KK : KK / 2;  // 16-byte K loads per key row
     u32x4 kraw[NU][KW];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const char* krow = kpage + (size_t)(kslot + 4 * u + (j & 3)) * D * ELT;
+    for (int h = 0; h < NH; ++h) {
+      const int kslot = (T0 + 32 * h) % p.bs + kq8;     // an 8-token run never crosses a page
+      const char* krun = kc + (size_t)kphys[h] * block_stride + (size_t)kslot * D * ELT;
 #pragma unroll
-      for (int w = 0; w < KW; ++w)
-        kraw[u][w] = (KVT == KV_BF16) ? ld16(krow + (32 * w + 8 * qd) * 2) : ld16(krow + 64 * w + 16 * qd);
+      for (int e = 0; e < 2; ++e) {
+        const char* krow = krun + (4 * e + (j & 3)) * D * ELT;
+#pragma unroll
+        for (int w = 0; w < KW; ++w)
+          kraw[2 * h + e][w] = (KVT == KV_BF16) ? ld16(krow + (32 * w + 8 * qd) * 2) : ld16(krow + 64 * w + 16 * qd);
+      }
     }
-    const int vt = T0 + RUN * qd;                       // first token of the lane's V run
-    const int vslot = vt % p.bs;
-    const char* vpage = vc + ((size_t)vphys * p.Hkv + kvh) * page_elems * ELT;
-    constexpr int VW = RUN * ELT / 4;                   // dwords of one lane's V run per d row
-    uint32_t vraw[NB][VW];
+    // V: 8 consecutive tokens of one d row per lane and d block (16 bytes bf16, 8 bytes fp8).
+    vword vraw[NH][NB];
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const char* vrow = vpage + ((size_t)(16 * n + j) * p.bs + vslot) * ELT;
-      if constexpr (VW == 8) {
-        const u32x4 w0 = ld16(vrow), w1 = ld16(vrow + 16);
+    for (int h = 0; h < NH; ++h) {
+      const int vslot = (T0 + 32 * h) % p.bs + vq8;
+      const char* vrun = vc + (size_t)vphys[h] * block_stride + ((size_t)j * p.bs + vslot) * ELT;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { vraw[n][e] = w0[e]; vraw[n][4 + e] = w1[e]; }
-      } else if constexpr (VW == 4) {
-        const u32x4 w0 = ld16(vrow);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vraw[n][e] = w0[e];
-      } else {
-        const u32x2 w0 = ld8(vrow);
-        vraw[n][0] = w0[0];
-        vraw[n][1] = w0[1];
+      for (int n = 0; n < NB; ++n) {
+        const char* vrow = vrun + (size_t)16 * n * p.bs * ELT;
+        if constexpr (KVT == KV_BF16) vraw[h][n] = ld16(vrow);
+        else vraw[h][n] = ld8(vrow);
       }
     }
     // ---------------- block-table entries of this wave's next chunk
     const int Tn = T0 + 4 * CH;
     if (Tn < t_end) {
-      kphys = table[k_block(Tn)];
-      vphys = table[v_block(Tn)];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        kphys[h] = table[k_block(Tn, h)];
+        vphys[h] = table[v_block(Tn, h)];
+      }
     }
 
-    // ---------------- S^T = K . Q^T for the NU sub-tiles; mask; chunk max.
+    // ---------------- S^T = K . Q^T for the NU sub-tiles, in exponent units t = c * s.
     f32x4 st[NU];
-    float mloc = kNegInf;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (KVT == KV_BF16) {
+      if constexpr (KVT == KV_BF16) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) a = mfma_16x16x32(bitcast<bf16x8>(kraw[u][kk]), qB[kk], a);
       } else {
@@ -196,90 +243,111 @@ __device__ __forceinline__ void decode_unit(const PagedParams& p, int b, int kvh
           a = mfma_16x16x32(fp8x8_to_bf16x8(kraw[u][w][2], kraw[u][w][3]), qB[2 * w + 1], a);
         }
       }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int tok = T0 + RUN * qd + 4 * u + s;
-        a[s] = (tok <= limit) ? a[s] : kNegInf;
-        mloc = fmaxf(mloc, a[s]);
-      }
-      st[u] = a;
+      st[u] = a * c;
     }
-    const float m_new = fmaxf(m, max_over_quads(mloc));
-    const float base = (m_new == kNegInf) ? 0.f : m_new * c;
-    const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m * c - base);
-    m = m_new;
-
-    // ---------------- P = exp2(c*s - c*m), running sum.
-    // P is rounded to bf16 for the MFMA. On the request's last chunk (the only chunk of a short
-    // request) P is carried as hi + lo bf16 parts, so that its rounding does not dominate the
-    // output error when only a few keys exist.
-    const bool split_p = (T0 + CH >= len);
-    bf16x4 pB[NU], pL[NU];
-    float psum = 0.f;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      f32x4 pv;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        pv[s] = fast_exp2(__builtin_fmaf(st[u][s], c, -base));
-        psum += pv[s];
-      }
-      pB[u] = f32x4_to_bf16x4(pv);
-      f32x4 lo;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) lo[s] = pv[s] - (float)pB[u][s];
-      pL[u] = f32x4_to_bf16x4(lo);
-    }
-    l = l * alpha + psum;
-
-    // ---------------- V^T operands; keys past the end of the request are zeroed (their P is
-    // zero, but the slots may hold anything, including NaN).
-    const int vvalid = len - vt;                        // tokens of the lane's run that exist
-    // ---------------- O^T = alpha * O^T + V^T . P^T
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      acc[n] *= alpha;
+    // A chunk is a tail chunk when some row may not see all of its keys (the end of the request,
+    // or the causal edge of a multi-token request). Only tail chunks mask scores, zero V slots
+    // past the end, and carry P as hi + lo bf16 parts: there rows see few keys, so the rounding
+    // of P would not average out.
+    const bool tail = (T0 + CH - 1 > min_limit);
+    if (tail) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        bf16x4 va;
-        if (KVT == KV_BF16) {
-          va = bitcast<bf16x4>(u32x2{vraw[n][2 * u], vraw[n][2 * u + 1]});
-        } else {
-          va = fp8x4_to_bf16x4(vraw[n][u]);
-        }
-        if (vvalid < RUN) {
+        const int tok0 = T0 + 32 * (u >> 1) + 8 * qd + 4 * (u & 1);
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            if (4 * u + s >= vvalid) va[s] = (bf16)0.f;
+        for (int s = 0; s < 4; ++s) st[u][s] = (tok0 + s <= limit) ? st[u][s] : kNegInf;
+      }
+    }
+    float mloc = kNegInf;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) mloc = fmaxf(fmaxf(mloc, fmaxf(st[u][0], st[u][1])), fmaxf(st[u][2], st[u][3]));
+    mloc = max_over_quads(mloc);
+    // Move the reference (and rescale what was accumulated) only where the new maximum is
+    // more than kLazyRescale above it; the first visible chunk of a row always moves it.
+    const bool move = mloc > mc + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      const float alpha = move ? ((mc == kNegInf) ? 0.f : fast_exp2(mc - mloc)) : 1.f;
+      mc = move ? mloc : mc;
+      l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) acc[n] *= alpha;
+    }
+    const float base = (mc == kNegInf) ? 0.f : mc;
+
+    // ---------------- P = 2^(t - mc), running sum, O^T += V^T . P^T (16x16x32 per d block, half)
+    if (!tail) {
+      bf16x8 pB[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          const float e0 = fast_exp2(st[2 * h + (t >> 2)][t & 3] - base);
+          const float e1 = fast_exp2(st[2 * h + (t >> 2)][(t & 3) + 1] - base);
+          l += e0 + e1;
+          pB[h][t] = (bf16)e0;
+          pB[h][t + 1] = (bf16)e1;
         }
-        acc[n] = mfma_16x16x16(va, pB[u], acc[n]);
-        if (split_p) acc[n] = mfma_16x16x16(va, pL[u], acc[n]);
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          bf16x8 va;
+          if constexpr (KVT == KV_BF16) va = bitcast<bf16x8>(vraw[h][n]);
+          else va = fp8x8_to_bf16x8(vraw[h][n][0], vraw[h][n][1]);
+          acc[n] = mfma_16x16x32(va, pB[h], acc[n]);
+        }
+    } else {
+      bf16x8 pB[NH], pL[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float e = fast_exp2(st[2 * h + (t >> 2)][t & 3] - base);
+          l += e;
+          pB[h][t] = (bf16)e;
+          pL[h][t] = (bf16)(e - (float)pB[h][t]);
+        }
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        // Keys past the end of the request are zeroed in V (their P is zero, but the slots may
+        // hold anything, including NaN).
+        const int vvalid = len - (T0 + 32 * h + 8 * qd);  // tokens of the lane's run that exist
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          bf16x8 va;
+          if constexpr (KVT == KV_BF16) va = bitcast<bf16x8>(vraw[h][n]);
+          else va = fp8x8_to_bf16x8(vraw[h][n][0], vraw[h][n][1]);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) va[t] = (t < vvalid) ? va[t] : (bf16)0.f;
+          acc[n] = mfma_16x16x32(va, pB[h], acc[n]);
+          acc[n] = mfma_16x16x32(va, pL[h], acc[n]);
+        }
       }
     }
   }
 
   // ---------------- combine the four waves (fixed order) through LDS.
-  // lds layout: stats[2][4][16] (max, sum) then O[4][R][D].
+  // lds layout: stats[2][4][16] (reference maximum, sum) then O[4][R][D].
   float* smax = lds;
   float* ssum = lds + 64;
   float* so = lds + 128;
   const float l_row = sum_over_quads(l);
   if (qd == 0) {
-    smax[wave * 16 + j] = m;
+    smax[wave * 16 + j] = mc;
     ssum[wave * 16 + j] = l_row;
   }
   __syncthreads();
   float mx = kNegInf;
 #pragma unroll
   for (int w = 0; w < 4; ++w) mx = fmaxf(mx, smax[w * 16 + j]);
-  const float mbase = (mx == kNegInf) ? 0.f : mx * c;
+  const float mbase = (mx == kNegInf) ? 0.f : mx;
   float ltot = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const float mw = smax[w * 16 + j];
-    ltot += (mw == kNegInf) ? 0.f : ssum[w * 16 + j] * fast_exp2(mw * c - mbase);
+    ltot += (mw == kNegInf) ? 0.f : ssum[w * 16 + j] * fast_exp2(mw - mbase);
   }
-  const float own = (m == kNegInf || ltot == 0.f) ? 0.f : fast_exp2(m * c - mbase) * vscale / ltot;
+  const float own = (mc == kNegInf || ltot == 0.f) ? 0.f : fast_exp2(mc - mbase) * vscale / ltot;
   if (j < R) {
     float* dst = so + ((size_t)wave * R + j) * D;
 #pragma unroll
@@ -287,7 +355,7 @@ __device__ __forceinline__ void decode_unit(const PagedParams& p, int b, int kvh
   }
   __syncthreads();
 
-  const float row_lse = (ltot == 0.f) ? kNegInf : kLn2 * (mx * c + fast_log2(ltot));
+  const float row_lse = (ltot == 0.f) ? kNegInf : kLn2 * (mx + fast_log2(ltot));
   if (direct) {
     for (int idx = tid; idx < R * (D / 4); idx += blockDim.x) {
       const int r = idx / (D / 4), d4 = 4 * (idx - r * (D / 4));
@@ -301,70 +369,169 @@ __device__ __forceinline__ void decode_unit(const PagedParams& p, int b, int kvh
       const int i = j / p.g, h = kvh * p.g + j % p.g;
       p.lse[(size_t)(q0 + i) * p.Hq + h] = row_lse;
     }
-  } else {
-    const size_t unit = ((size_t)b * p.Hkv + kvh) * p.num_splits + split;
-    float* wo = p.ws_o + unit * 16 * D;
-    for (int idx = tid; idx < R * (D / 4); idx += blockDim.x) {
-      const int r = idx / (D / 4), d4 = 4 * (idx - r * (D / 4));
-      f32x4 o = *reinterpret_cast<const f32x4*>(so + (0 * R + r) * D + d4);
+    return;
+  }
+  const size_t unit = (size_t)blockIdx.x * 2 + slot;
+  float* wo = p.ws_o + unit * 16 * D;
+  for (int idx = tid; idx < R * (D / 4); idx += blockDim.x) {
+    const int r = idx / (D / 4), d4 = 4 * (idx - r * (D / 4));
+    f32x4 o = *reinterpret_cast<const f32x4*>(so + (0 * R + r) * D + d4);
 #pragma unroll
-      for (int w = 1; w < 4; ++w) o += *reinterpret_cast<const f32x4*>(so + (w * R + r) * D + d4);
-      *reinterpret_cast<f32x4*>(wo + r * D + d4) = o;
-    }
-    if (wave == 0 && qd == 0 && j < R) p.ws_lse[unit * 16 + j] = row_lse;
+    for (int w = 1; w < 4; ++w) o += *reinterpret_cast<const f32x4*>(so + (w * R + r) * D + d4);
+    *reinterpret_cast<f32x4*>(wo + r * D + d4) = o;
+  }
+  if (wave == 0 && qd == 0 && j < R) p.ws_lse[unit * 16 + j] = row_lse;
+}
+
+// Exclusive prefix sums of the per-request chunk counts into sp[0 .. B] (LDS), by all 256
+// threads; thread t scans a contiguous segment of requests. Ends with a barrier.
+template <int CH>
+__device__ __forceinline__ void chunk_prefix(const PagedParams& p, int* sp, int* wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = p.num_seqs;
+  const int per = (B + 255) / 256;
+  const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) local += decode_chunks<CH>(p, b);
+  int incl = local;                                    // inclusive scan over the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int off = incl - local;
+  for (int w = 0; w < wave; ++w) off += wave_tot[w];
+  for (int b = b0; b < b1; ++b) {
+    sp[b] = off;
+    off += decode_chunks<CH>(p, b);
+  }
+  if (tid == 255) sp[B] = off;
+  __syncthreads();
+}
+
+// The partition kernel's body: workgroup blockIdx.x takes its share of the batch's chunks and
+// walks the (request, kv head) pieces it covers. lds: the combine buffer of decode_piece, then
+// sp[B + 1] and 4 scratch ints.
+template <int D, int KVT, int NU>
+__device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, int combine_floats) {
+  constexpr int CH = DecodeShape<NU>::CH;
+  int* sp = reinterpret_cast<int*>(lds + combine_floats);
+  int* wave_tot = sp + p.num_seqs + 1;
+  chunk_prefix<CH>(p, sp, wave_tot);
+  const int B = p.num_seqs, G = p.num_wg, g = blockIdx.x;
+  if (g == 0)
+    for (int b = threadIdx.x; b <= B; b += blockDim.x) p.ws_prefix[b] = sp[b];
+  const long long T = (long long)p.Hkv * sp[B];
+  const long long r0 = share_start(g, T, G), r1 = share_start(g + 1, T, G);
+  if (r0 >= r1) return;
+  // request holding chunk r0: the largest b < B with Hkv * sp[b] <= r0
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((long long)p.Hkv * sp[mid] <= r0) lo = mid; else hi = mid - 1;
+  }
+  int b = lo;
+  long long pos = r0;
+  bool first = true;
+  const int wave = threadIdx.x >> 6;
+  while (pos < r1) {
+    const int nb = sp[b + 1] - sp[b];
+    if (nb == 0) { ++b; continue; }
+    const long long base = (long long)p.Hkv * sp[b];
+    const int kvh = (int)((pos - base) / nb);
+    const int c0 = (int)(pos - base - (long long)kvh * nb);
+    const int c1 = (int)min((long long)nb, c0 + (r1 - pos));
+    // chunks are dealt to the waves round-robin over the whole share
+    const int wave_first = (int)((wave - (pos - r0) % 4 + 4) % 4);
+    const int slot = (c0 == 0 && c1 == nb) ? -1 : (first ? 0 : 1);
+    decode_piece<D, KVT, NU>(p, b, kvh, c0, c1, wave_first, slot, lds);
+    pos += c1 - c0;
+    first = false;
+    if (c1 == nb && kvh == p.Hkv - 1) ++b;
   }
 }
 
-// Merge of the partitions of one (request, kv head, row): natural-log LSE weights
-// ("Attention kernels", section "Prefill and decode attention": partial results combined the
-// same way as the online softmax). 256 threads: thread t sums d-quad t % (D/4) over the
-// partitions s = t / (D/4), t / (D/4) + 256/(D/4), ...; the groups are then added in LDS in a
-// fixed order. lds: weights[num_splits] then sums[256/(D/4)][D].
-template <int D>
+// Merge of the pieces of one (request, kv head, row) that spans several shares, with
+// natural-log LSE weights ("Attention kernels", section "Prefill and decode attention": partial
+// results combined the same way as the online softmax). Also writes out = 0, lse = -inf for
+// rows of a request with no key. Latency-bound, so every phase issues all of its loads at once:
+// (1) the pieces' LSEs into LDS, (2) the weights, (3) thread t sums d-quad t % (D/4) over the
+// pieces t / (D/4) + k * 256/(D/4), eight loads in flight, and the groups are added in LDS in a
+// fixed order. lds: lse/weights[G] then sums[256/(D/4)][D].
+template <int D, int CH>
 __device__ __forceinline__ void merge_row(const PagedParams& p, int b, int kvh, int r, float* lds) {
   constexpr int DQ = D / 4;
   constexpr int GROUPS = 256 / DQ;
-  const int len = p.seq_lens_k[b];
   const int q0 = p.cu_seqlens_q ? p.cu_seqlens_q[b] : b;
   const int qlen = p.cu_seqlens_q ? (p.cu_seqlens_q[b + 1] - q0) : 1;
   const int R = qlen * p.g;
-  if (R > 16 || r >= R) return;                        // rows written by other paths
-  const int C = p.split_tokens;
-  const int ns = (len + C - 1) / C;
-  if (ns <= 1) return;                                 // written directly by the partition kernel
-  const int tid = threadIdx.x;
-  const size_t unit0 = ((size_t)b * p.Hkv + kvh) * p.num_splits;
+  if (R > 16 || r >= R) return;                        // rows of another path, or no such row
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int i = r / p.g, h = kvh * p.g + r % p.g;
+  bf16* orow = p.out + ((size_t)(q0 + i) * p.Hq + h) * D;
+  const int nb = p.ws_prefix[b + 1] - p.ws_prefix[b];
+  if (nb == 0) {                                       // no key at all
+    if (tid < DQ) *reinterpret_cast<bf16x4*>(orow + 4 * tid) = bf16x4{};
+    if (p.lse && tid == 0) p.lse[(size_t)(q0 + i) * p.Hq + h] = kNegInf;
+    return;
+  }
+  const int G = p.num_wg;
+  const long long T = (long long)p.Hkv * p.ws_prefix[p.num_seqs];
+  const long long start = (long long)p.Hkv * p.ws_prefix[b] + (long long)kvh * nb;
+  const int g_lo = share_of(start, T, G), g_hi = share_of(start + nb - 1, T, G);
+  if (g_lo == g_hi) return;                            // written directly by the partition kernel
+  const int ns = g_hi - g_lo + 1;
+  // piece k lives in share g_lo + k: slot 0 (the unit is that share's first unit) except for the
+  // first piece when the unit began inside share g_lo's range after another unit. Empty shares
+  // (when there are fewer chunk groups than shares) hold no piece and get weight 0.
+  const int slot_lo = (share_start(g_lo, T, G) == start) ? 0 : 1;
+  auto piece = [&](int k) { return (size_t)(g_lo + k) * 2 + (k == 0 ? slot_lo : 0); };
   float* w = lds;
-  float* red = lds + p.num_splits;
+  float* red = lds + G;
   __shared__ float s_max, s_sum;
+  for (int k = tid; k < ns; k += 256) {
+    const bool has = share_start(g_lo + k, T, G) < share_start(g_lo + k + 1, T, G);
+    w[k] = has ? p.ws_lse[piece(k) * 16 + r] : kNegInf;
+  }
+  __syncthreads();
   if (tid < 64) {
     float mx = kNegInf;
-    for (int s = tid; s < ns; s += 64) mx = fmaxf(mx, p.ws_lse[(unit0 + s) * 16 + r]);
+    for (int k = lane; k < ns; k += 64) mx = fmaxf(mx, w[k]);
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
     float sum = 0.f;
-    for (int s = tid; s < ns; s += 64) {
-      const float ls = p.ws_lse[(unit0 + s) * 16 + r];
+    for (int k = lane; k < ns; k += 64) {
+      const float ls = w[k];
       const float e = (mx == kNegInf || ls == kNegInf) ? 0.f : fast_exp2((ls - mx) * kLog2e);
-      w[s] = e;
+      w[k] = e;
       sum += e;
     }
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-    if (tid == 0) { s_max = mx; s_sum = sum; }
+    if (lane == 0) { s_max = mx; s_sum = sum; }
   }
   __syncthreads();
   const int dq = tid % DQ, grp = tid / DQ;
+  const float* src = p.ws_o + (size_t)r * D + 4 * dq;
   f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = grp; s < ns; s += GROUPS) {
-    const f32x4 os = *reinterpret_cast<const f32x4*>(p.ws_o + ((unit0 + s) * 16 + r) * D + 4 * dq);
-    o += os * w[s];
+  for (int k0 = grp; k0 < ns; k0 += 8 * GROUPS) {
+    f32x4 part[8];
+    float wk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u * GROUPS;
+      wk[u] = (k < ns) ? w[k] : 0.f;
+      part[u] = (wk[u] != 0.f) ? *reinterpret_cast<const f32x4*>(src + piece(k) * 16 * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o += part[u] * wk[u];
   }
   *reinterpret_cast<f32x4*>(red + grp * D + 4 * dq) = o;
   __syncthreads();
   if (grp == 0) {
     for (int g2 = 1; g2 < GROUPS; ++g2) o += *reinterpret_cast<const f32x4*>(red + g2 * D + 4 * dq);
     const float inv = (s_sum > 0.f) ? 1.f / s_sum : 0.f;
-    const int i = r / p.g, h = kvh * p.g + r % p.g;
-    *reinterpret_cast<bf16x4*>(p.out + ((size_t)(q0 + i) * p.Hq + h) * D + 4 * dq) = f32x4_to_bf16x4(o * inv);
+    *reinterpret_cast<bf16x4*>(orow + 4 * dq) = f32x4_to_bf16x4(o * inv);
     if (p.lse && dq == 0)
       p.lse[(size_t)(q0 + i) * p.Hq + h] = (s_sum > 0.f) ? s_max + kLn2 * fast_log2(s_sum) : kNegInf;
   }

@@ -12,10 +12,15 @@ namespace attn {
 // walked heaviest (last) first.
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, hipStream_t stream);
 
-// Split-KV paged decode (grid: partitions x kv heads x requests), followed, when there is more
-// than one partition, by the LSE merge (grid: rows x kv heads x requests). rows_max = rows per
-// (request, kv head) (<= 16); it sizes the LDS combine buffer and the merge grid.
+// Split-KV paged decode: p.num_wg partition workgroups, each taking an equal share of the batch's
+// (request, kv head, key chunk) work, then the LSE merge (grid: rows x kv heads x requests).
+// rows_max = rows per (request, kv head) (<= 16); it sizes the LDS combine buffer and the merge
+// grid.
 hipError_t launch_decode(const PagedParams& p, int head_dim, int kv_type, int rows_max, hipStream_t stream);
+
+// Keys per chunk of the decode variant, and its resident workgroups per compute unit.
+int decode_chunk_tokens(int head_dim, int kv_type);
+int decode_wgs_per_cu(int head_dim, int kv_type);
 
 // Number of CUs of the current device (cached per device).
 int device_cu_count();

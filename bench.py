@@ -87,8 +87,8 @@ def decode_section(lib, case, splits, steps, warmup, label):
     b, hq, d = case.q.shape
     hkv, bs = case.num_kv_heads, case.block_size
     maxblk = case.block_table.shape[1]
-    s = lib.attn_decode_num_splits(b, hkv, bs, maxblk, splits)
-    ws = torch.empty(max(1, lib.attn_decode_workspace_bytes(b, hkv, d, s)), dtype=torch.uint8, device=case.q.device)
+    s = lib.attn_decode_num_splits(b, hkv, d, 0 if case.kv_format == "bf16" else 1, bs, maxblk, splits)
+    ws = torch.zeros(max(1, lib.attn_decode_workspace_bytes(b, hkv, d, s)), dtype=torch.uint8, device=case.q.device)
     out = torch.empty_like(case.q)
     lse = torch.empty((b, hq), dtype=torch.float32, device=case.q.device)
 

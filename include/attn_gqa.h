@@ -35,7 +35,8 @@
  *       t % block_size of logical block t / block_size ("Optimization 1",
  *       section 3.4 PagedAttention; "Attention kernels", section "Paged KV and kernels").
  *   - head_dim must be 128 or 256; num_q_heads must be a multiple of
- *     num_kv_heads; block_size must be 16, 32, 64, 128 or 256.
+ *     num_kv_heads; block_size must be 16, 32, 64, 128 or 256; paged calls
+ *     take at most 16384 requests.
  *   - stream is a hipStream_t (NULL = the default stream). Calls return once
  *     the work is enqueued; results are valid after the stream synchronises.
  *   - Argument validation is synchronous and happens before anything is
@@ -91,20 +92,25 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v,
                                 void* stream);
 
 /*
- * Number of KV partitions a paged decode call will use (split-KV, "Attention
- * kernels", section "Prefill and decode attention"). requested > 0 is
- * returned clamped to the number of 64-key chunks of the longest possible
- * request (max_blocks_per_seq * block_size keys) and to 4096; requested == 0
- * picks one from the batch shape and the device's compute-unit count. Returns 0 on invalid sizes.
+ * Number of partitions (partition workgroups) a paged decode call will use
+ * (split-KV, "Attention kernels", section "Prefill and decode attention").
+ * The batch's work -- every (request, kv head, chunk of keys) -- is cut into
+ * that many equal contiguous shares, so each partition streams the same number
+ * of KV bytes whatever the mix of context lengths; a request whose keys span
+ * several shares is merged from their partial results. requested > 0 is
+ * returned clamped to the useful count (at most one share per 4 chunks of the
+ * largest possible batch) and to 4096; requested == 0 picks one partition per
+ * resident workgroup slot of the device (compute units x workgroups per unit
+ * for this head_dim and kv_dtype). Returns 0 on invalid arguments.
  */
-int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
-                               int32_t max_blocks_per_seq, int32_t requested);
+int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t kv_dtype,
+                               int32_t block_size, int32_t max_blocks_per_seq, int32_t requested);
 
 /*
  * Workspace bytes a paged decode / varlen-paged call needs for num_splits
- * (resolved, >= 1) partitions: per (request, kv head, partition) a block of
- * 16 rows x head_dim fp32 partial outputs plus 16 fp32 partial LSEs. 0 when
- * num_splits == 1. The contents need no initialisation; calls that share one
+ * (resolved, >= 1) partitions: two partial results per partition (16 rows x
+ * head_dim fp32 outputs plus 16 fp32 LSEs each) and num_seqs + 1 int32 chunk
+ * offsets. The contents need no initialisation; calls that share one
  * workspace must not overlap in time (enqueue them on one stream).
  */
 size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
@@ -114,10 +120,9 @@ size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32
  * Paged decode: one query token per request over its paged KV cache.
  * Each KV head is read once for all num_q_heads / num_kv_heads query heads of
  * its group ("Attention kernels", section "Prefill and decode attention"); the
- * key axis is cut into num_splits partitions of
- *   C = roundup(ceil(max_blocks_per_seq * block_size / num_splits), 64) tokens,
- * partition s covering keys [s*C, min((s+1)*C, seq_lens[b])), and the
- * partitions are merged with their log-sum-exps.
+ * key axis is split across num_splits partitions that take equal shares of
+ * the batch's keys (see attn_decode_num_splits), and the pieces of a request
+ * are merged with their log-sum-exps.
  *   q [num_seqs, num_q_heads, head_dim] bf16 (the newest token of each request)
  *   k_cache, v_cache: see the layouts above; kv_dtype ATTN_KV_BF16 or ATTN_KV_FP8_E4M3FN
  *   k_scale, v_scale [num_kv_heads] fp32 per-head dequantisation scales (fp8 only; ignored for bf16)
@@ -125,11 +130,11 @@ size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32
  *   number of cached tokens INCLUDING the current one (0 gives out 0, lse -inf)
  *   out [num_seqs, num_q_heads, head_dim] bf16; lse [num_seqs, num_q_heads] fp32 or NULL
  *   num_splits: 0 = automatic (attn_decode_num_splits), else the partition count
- *   workspace: device scratch of >= attn_decode_workspace_bytes(...) bytes
- *   (may be NULL when that is 0).
- * A request whose keys fit one partition is written directly; otherwise every
- * partition writes a normalised partial output and its LSE to the workspace,
- * and a second kernel, enqueued on the same stream, merges them.
+ *   workspace: device scratch of >= attn_decode_workspace_bytes(...) bytes.
+ * A (request, kv head) whose keys lie in one partition's share is written by
+ * that partition; otherwise each partition writes a normalised partial output
+ * and its LSE to the workspace, and a second kernel, enqueued on the same
+ * stream, merges them (it also writes the rows of requests with no key).
  * Requires num_q_heads / num_kv_heads <= 16.
  */
 attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,

@@ -70,7 +70,7 @@ def _decode(**kw):
     (dict(q=None), 1), (dict(kc=None), 1), (dict(table=None), 1), (dict(lens=None), 1), (dict(out=None), 1),
     (dict(kvt=1), 1),                               # fp8 without scales
     (dict(kvt=7), 3), (dict(d=96), 3), (dict(bs=8), 3), (dict(bs=48), 3), (dict(hq=64, hkv=2), 3),
-    (dict(nseq=-1), 2), (dict(hq=7), 2), (dict(nblk=0), 2), (dict(maxblk=0), 2), (dict(splits=-2), 2),
+    (dict(nseq=-1), 2), (dict(nseq=16385), 3), (dict(hq=7), 2), (dict(nblk=0), 2), (dict(maxblk=0), 2), (dict(splits=-2), 2),
     (dict(splits=2, maxblk=40), 4),                 # partials need a workspace
     (dict(splits=2, maxblk=40, ws=FAKE, wsb=16), 4),
 ])
@@ -80,12 +80,18 @@ def test_decode_validation(kw, code):
 
 def test_split_planning_and_workspace_sizes():
     lib = _lib.load()
-    assert lib.attn_decode_num_splits(2, 2, 64, 2048, 64) == 64
-    assert lib.attn_decode_num_splits(2, 2, 64, 2048, 100000) == 2048   # at most one per 64-key chunk
-    assert lib.attn_decode_num_splits(1, 1, 16, 1, 8) == 1
-    assert lib.attn_decode_num_splits(0, 1, 16, 1, 8) == 0
-    assert lib.attn_decode_workspace_bytes(2, 2, 128, 1) == 0
-    assert lib.attn_decode_workspace_bytes(2, 2, 128, 64) == 2 * 2 * 64 * 16 * 129 * 4
+    # (num_seqs, num_kv_heads, head_dim, kv_dtype, block_size, max_blocks_per_seq, requested)
+    assert lib.attn_decode_num_splits(2, 2, 128, 0, 64, 2048, 64) == 64
+    assert lib.attn_decode_num_splits(2, 2, 128, 0, 64, 2048, 100000) == 2048   # one share per 4 chunks
+    assert lib.attn_decode_num_splits(2, 2, 128, 0, 16, 8, 100000) == 2         # 4 units x 2 chunks
+    assert lib.attn_decode_num_splits(1, 1, 128, 1, 16, 1, 8) == 1
+    assert lib.attn_decode_num_splits(64, 8, 256, 0, 256, 4096, 100000) == 4096  # at most 4096
+    assert lib.attn_decode_num_splits(0, 1, 128, 0, 16, 1, 8) == 0
+    assert lib.attn_decode_num_splits(1, 1, 96, 0, 16, 1, 8) == 0               # head_dim
+    assert lib.attn_decode_num_splits(1, 1, 128, 5, 16, 1, 8) == 0              # kv dtype
+    assert lib.attn_decode_workspace_bytes(2, 2, 128, 1) == 2 * 16 * 129 * 4 + 3 * 4
+    assert lib.attn_decode_workspace_bytes(2, 2, 128, 64) == 64 * 2 * 16 * 129 * 4 + 3 * 4
+    assert lib.attn_decode_workspace_bytes(2, 2, 128, 0) == 0
 
 
 def test_varlen_validation():
