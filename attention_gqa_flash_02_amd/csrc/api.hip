@@ -82,7 +82,7 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v, con
   p.q = static_cast<const bf16*>(q);
   p.k = static_cast<const bf16*>(k);
   p.v = static_cast<const bf16*>(v);
-  p.cu_seqlens = cu_seqlens;
+  p.cu_seqlens_q = cu_seqlens;
   p.out = static_cast<bf16*>(out);
   p.lse = lse;
   p.scale = scale;
@@ -205,11 +205,61 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
   if (total_q < 0 || max_q_len < 0 || max_q_len > total_q || (causal != 0 && causal != 1) ||
       !std::isfinite(scale))
     return ATTN_ERR_SHAPE;
-  (void)workspace;
-  (void)workspace_bytes;
-  (void)stream;
-  (void)lse;
-  return ATTN_ERR_UNSUPPORTED;  // mixed launch not built yet
+  if ((long long)total_q * num_q_heads * head_dim > (long long)INT_MAX * 8) return ATTN_ERR_SHAPE;
+  const int S = attn_decode_num_splits(num_seqs, num_kv_heads, head_dim, kv_dtype, block_size,
+                                       max_blocks_per_seq, num_splits);
+  const size_t need = attn_varlen_workspace_bytes(num_seqs, num_kv_heads, head_dim, S);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (total_q == 0) return ATTN_OK;
+  const int g = num_q_heads / num_kv_heads;
+  const int kvt = kv_dtype == ATTN_KV_BF16 ? KV_BF16 : KV_FP8;
+
+  PagedParams dp{};
+  dp.q = static_cast<const bf16*>(q);
+  dp.k_cache = k_cache;
+  dp.v_cache = v_cache;
+  dp.k_scale = k_scale;
+  dp.v_scale = v_scale;
+  dp.block_table = block_table;
+  dp.seq_lens_k = seq_lens_k;
+  dp.cu_seqlens_q = cu_seqlens_q;
+  dp.out = static_cast<bf16*>(out);
+  dp.lse = lse;
+  dp.ws_o = static_cast<float*>(workspace);
+  dp.ws_lse = dp.ws_o + (size_t)S * 2 * 16 * head_dim;
+  dp.ws_prefix = reinterpret_cast<int32_t*>(dp.ws_lse + (size_t)S * 2 * 16);
+  dp.scale = scale;
+  dp.num_seqs = num_seqs;
+  dp.Hq = num_q_heads;
+  dp.Hkv = num_kv_heads;
+  dp.g = g;
+  dp.bs = block_size;
+  dp.max_blocks = max_blocks_per_seq;
+  dp.num_wg = S;
+  dp.causal = causal;
+
+  PrefillParams pp{};
+  pp.q = dp.q;
+  pp.out = dp.out;
+  pp.lse = lse;
+  pp.cu_seqlens_q = cu_seqlens_q;
+  pp.k_cache = k_cache;
+  pp.v_cache = v_cache;
+  pp.k_scale = kvt == KV_FP8 ? k_scale : nullptr;
+  pp.v_scale = kvt == KV_FP8 ? v_scale : nullptr;
+  pp.block_table = block_table;
+  pp.seq_lens_k = seq_lens_k;
+  pp.scale = scale;
+  pp.num_seqs = num_seqs;
+  pp.Hq = num_q_heads;
+  pp.Hkv = num_kv_heads;
+  pp.g = g;
+  pp.hpw = gcd_int(g, 4);
+  pp.causal = causal;
+  pp.bs = block_size;
+  pp.max_blocks = max_blocks_per_seq;
+  hipError_t e = launch_mixed(pp, dp, head_dim, kvt, total_q, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 }  // extern "C"

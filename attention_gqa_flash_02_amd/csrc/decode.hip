@@ -6,7 +6,7 @@ namespace attn {
 template <int D, int KVT, int NU>
 __global__ __launch_bounds__(256) void decode_share_kernel(PagedParams p, int combine_floats) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  decode_share<D, KVT, NU>(p, reinterpret_cast<float*>(smem_raw), combine_floats);
+  decode_share<D, KVT, NU>(p, reinterpret_cast<float*>(smem_raw), combine_floats, blockIdx.x);
 }
 
 template <int D, int CH>
@@ -32,18 +32,30 @@ static hipError_t launch_decode_t(const PagedParams& p, int rows_max, hipStream_
   hipLaunchKernelGGL((decode_share_kernel<D, KVT, NU>), dim3(p.num_wg), dim3(256), lds, stream, p, combine_floats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int CH = DecodeShape<NU>::CH;
+  return launch_decode_merge(p, D, NU, rows_max, stream);
+}
+
+template <int D, int CH>
+static hipError_t launch_merge_t(const PagedParams& p, int rows_max, hipStream_t stream) {
   const size_t merge_lds = ((size_t)p.num_wg + (256 / (D / 4)) * D) * sizeof(float);
   static size_t merge_lds_set = 0;
   if (merge_lds > merge_lds_set) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_merge_kernel<D, CH>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)merge_lds);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_merge_kernel<D, CH>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)merge_lds);
     if (e != hipSuccess) return e;
     merge_lds_set = merge_lds;
   }
   dim3 mgrid(rows_max, p.Hkv, p.num_seqs);
   hipLaunchKernelGGL((decode_merge_kernel<D, CH>), mgrid, dim3(256), merge_lds, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const PagedParams& p, int head_dim, int nu, int rows_max, hipStream_t stream) {
+  if (head_dim == 128 && nu == 4) return launch_merge_t<128, 64>(p, rows_max, stream);
+  if (head_dim == 128 && nu == 2) return launch_merge_t<128, 32>(p, rows_max, stream);
+  if (head_dim == 256 && nu == 4) return launch_merge_t<256, 64>(p, rows_max, stream);
+  if (head_dim == 256 && nu == 2) return launch_merge_t<256, 32>(p, rows_max, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const PagedParams& p, int head_dim, int kv_type, int rows_max, hipStream_t stream) {

@@ -101,7 +101,7 @@ struct DecodeShape {
 // else it is written to partial slot `slot` of the workspace.
 template <int D, int KVT, int NU>
 __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kvh, int c0, int c1, int wave_first,
-                                             int slot, float* lds) {
+                                             int share, int slot, float* lds) {
   constexpr int CH = DecodeShape<NU>::CH;
   constexpr int NH = DecodeShape<NU>::NH;
   constexpr int KK = D / 32;        // QK MFMAs per 16-key sub-tile
@@ -371,7 +371,7 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
     }
     return;
   }
-  const size_t unit = (size_t)blockIdx.x * 2 + slot;
+  const size_t unit = (size_t)share * 2 + slot;
   float* wo = p.ws_o + unit * 16 * D;
   for (int idx = tid; idx < R * (D / 4); idx += blockDim.x) {
     const int r = idx / (D / 4), d4 = 4 * (idx - r * (D / 4));
@@ -383,16 +383,15 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
   if (wave == 0 && qd == 0 && j < R) p.ws_lse[unit * 16 + j] = row_lse;
 }
 
-// Exclusive prefix sums of the per-request chunk counts into sp[0 .. B] (LDS), by all 256
+// Exclusive prefix sums of count(b) over requests b < B into sp[0 .. B] (LDS), by all 256
 // threads; thread t scans a contiguous segment of requests. Ends with a barrier.
-template <int CH>
-__device__ __forceinline__ void chunk_prefix(const PagedParams& p, int* sp, int* wave_tot) {
+template <class Count>
+__device__ __forceinline__ void block_prefix(int B, Count count, int* sp, int* wave_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int B = p.num_seqs;
   const int per = (B + 255) / 256;
   const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
   int local = 0;
-  for (int b = b0; b < b1; ++b) local += decode_chunks<CH>(p, b);
+  for (int b = b0; b < b1; ++b) local += count(b);
   int incl = local;                                    // inclusive scan over the wave
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -405,22 +404,21 @@ __device__ __forceinline__ void chunk_prefix(const PagedParams& p, int* sp, int*
   for (int w = 0; w < wave; ++w) off += wave_tot[w];
   for (int b = b0; b < b1; ++b) {
     sp[b] = off;
-    off += decode_chunks<CH>(p, b);
+    off += count(b);
   }
   if (tid == 255) sp[B] = off;
   __syncthreads();
 }
 
-// The partition kernel's body: workgroup blockIdx.x takes its share of the batch's chunks and
-// walks the (request, kv head) pieces it covers. lds: the combine buffer of decode_piece, then
-// sp[B + 1] and 4 scratch ints.
+// The partition kernel's body: share g of the batch's chunks walks the (request, kv head)
+// pieces it covers. lds: the combine buffer of decode_piece, then sp[B + 1] and 4 scratch ints.
 template <int D, int KVT, int NU>
-__device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, int combine_floats) {
+__device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, int combine_floats, int g) {
   constexpr int CH = DecodeShape<NU>::CH;
   int* sp = reinterpret_cast<int*>(lds + combine_floats);
   int* wave_tot = sp + p.num_seqs + 1;
-  chunk_prefix<CH>(p, sp, wave_tot);
-  const int B = p.num_seqs, G = p.num_wg, g = blockIdx.x;
+  block_prefix(p.num_seqs, [&](int b) { return decode_chunks<CH>(p, b); }, sp, wave_tot);
+  const int B = p.num_seqs, G = p.num_wg;
   if (g == 0)
     for (int b = threadIdx.x; b <= B; b += blockDim.x) p.ws_prefix[b] = sp[b];
   const long long T = (long long)p.Hkv * sp[B];
@@ -446,7 +444,7 @@ __device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, i
     // chunks are dealt to the waves round-robin over the whole share
     const int wave_first = (int)((wave - (pos - r0) % 4 + 4) % 4);
     const int slot = (c0 == 0 && c1 == nb) ? -1 : (first ? 0 : 1);
-    decode_piece<D, KVT, NU>(p, b, kvh, c0, c1, wave_first, slot, lds);
+    decode_piece<D, KVT, NU>(p, b, kvh, c0, c1, wave_first, g, slot, lds);
     pos += c1 - c0;
     first = false;
     if (c1 == nb && kvh == p.Hkv - 1) ++b;

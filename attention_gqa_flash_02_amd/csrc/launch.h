@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "decode_core.h"
 #include "prefill_core.h"
 
@@ -17,6 +19,15 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, 
 // rows_max = rows per (request, kv head) (<= 16); it sizes the LDS combine buffer and the merge
 // grid.
 hipError_t launch_decode(const PagedParams& p, int head_dim, int kv_type, int rows_max, hipStream_t stream);
+
+// The LSE merge alone (the second launch of a paged decode / mixed call); nu = the partition
+// kernel's sub-tiles per chunk (chunk = 16 * nu keys).
+hipError_t launch_decode_merge(const PagedParams& p, int head_dim, int nu, int rows_max, hipStream_t stream);
+
+// Mixed varlen batch over a paged cache: one launch holding the decode path's p.num_wg shares
+// and the prefill q-tiles, then the merge.
+hipError_t launch_mixed(const PrefillParams& pp, const PagedParams& dp, int head_dim, int kv_type, int total_q,
+                        hipStream_t stream);
 
 // Keys per chunk of the decode variant, and its resident workgroups per compute unit.
 int decode_chunk_tokens(int head_dim, int kv_type);

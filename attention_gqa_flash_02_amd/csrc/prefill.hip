@@ -1,13 +1,52 @@
-// Prefill kernel instantiations and launcher.
+// Prefill and mixed-batch kernel instantiations and launchers.
 #include "launch.h"
 
 namespace attn {
 
+// Varlen self-attention over contiguous K/V. Grid: (head groups, requests, q-tiles), q-tiles
+// walked heaviest (last) first.
 template <int D, int BN>
 __global__ __launch_bounds__(256) void prefill_varlen_kernel(PrefillParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  prefill_tile_body<D, BN>(p, reinterpret_cast<bf16*>(smem_raw), blockIdx.x, blockIdx.y,
-                           p.num_qtiles - 1 - (int)blockIdx.z);
+  prefill_tile_body<D, BN, ContigLoader<D, BN>, false>(p, reinterpret_cast<bf16*>(smem_raw), blockIdx.x,
+                                                        blockIdx.y, p.num_qtiles - 1 - (int)blockIdx.z);
+}
+
+// Q-tiles of request b on the prefill path of a mixed batch (its rows do not fit the decode path).
+__device__ __forceinline__ int prefill_qtiles(const PrefillParams& p, int b, int tq) {
+  const int lq = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
+  return (lq * p.g > 16) ? (lq + tq - 1) / tq : 0;
+}
+
+// Mixed varlen batch over a paged cache in one launch: workgroups [0, n_dec) are the decode
+// path's shares (memory-bound; dispatched first so that they run beside the prefill tiles), the
+// rest are prefill q-tiles (compute-bound), heaviest tile of each request first.
+template <int D, int BN, int KVT, int NU>
+__global__ __launch_bounds__(256) void varlen_mixed_kernel(PrefillParams pp, PagedParams dp, int n_dec,
+                                                           int combine_floats) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  float* lds = reinterpret_cast<float*>(smem_raw);
+  if ((int)blockIdx.x < n_dec) {
+    decode_share<D, KVT, NU>(dp, lds, combine_floats, blockIdx.x);
+    return;
+  }
+  using Loader = PagedLoader<D, BN, KVT == KV_FP8>;
+  const int w = blockIdx.x - n_dec;
+  const int hg = pp.Hkv * (pp.g / pp.hpw);
+  const int hgrp = w % hg, t = w / hg;
+  const int tq = 32 * (4 / pp.hpw);
+  int* sp = reinterpret_cast<int*>(smem_raw + PrefillShape<D, BN>::LDS_BYTES);
+  block_prefix(pp.num_seqs, [&](int b) { return prefill_qtiles(pp, b, tq); }, sp, sp + pp.num_seqs + 1);
+  if (t >= sp[pp.num_seqs]) return;
+  int lo = 0, hi = pp.num_seqs - 1;                    // the largest b with sp[b] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sp[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int nt = sp[lo + 1] - sp[lo];
+  const int qt = nt - 1 - (t - sp[lo]);
+  __syncthreads();                                     // sp is not read below; the tile reuses LDS
+  prefill_tile_body<D, BN, Loader, true>(pp, reinterpret_cast<bf16*>(smem_raw), hgrp, lo, qt);
 }
 
 template <int D, int BN>
@@ -32,6 +71,39 @@ static hipError_t launch_prefill_t(const PrefillParams& p, int max_seqlen, hipSt
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, hipStream_t stream) {
   if (head_dim == 128) return launch_prefill_t<128, 64>(p, max_seqlen, stream);
   if (head_dim == 256) return launch_prefill_t<256, 32>(p, max_seqlen, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int D, int BN, int KVT, int NU>
+static hipError_t launch_mixed_t(const PrefillParams& pp, const PagedParams& dp, int total_q, hipStream_t stream) {
+  const int tq = 32 * (4 / pp.hpw);
+  // upper bound on prefill q-tiles: every request adds at most one partial tile
+  const long long n_pre = (long long)pp.Hkv * (pp.g / pp.hpw) * ((total_q + tq - 1) / tq + pp.num_seqs);
+  const int n_dec = dp.num_wg;
+  if (n_pre + n_dec > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int combine_floats = 128 + 4 * 16 * D;
+  const size_t ints = ((size_t)pp.num_seqs + 5) * sizeof(int);
+  const size_t lds = std::max((size_t)PrefillShape<D, BN>::LDS_BYTES, (size_t)combine_floats * sizeof(float)) + ints;
+  static size_t lds_set = 0;
+  if (lds > lds_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&varlen_mixed_kernel<D, BN, KVT, NU>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_set = lds;
+  }
+  hipLaunchKernelGGL((varlen_mixed_kernel<D, BN, KVT, NU>), dim3((unsigned)(n_pre + n_dec)), dim3(256), lds, stream,
+                     pp, dp, n_dec, combine_floats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_decode_merge(dp, D, NU, 16, stream);
+}
+
+hipError_t launch_mixed(const PrefillParams& pp, const PagedParams& dp, int head_dim, int kv_type, int total_q,
+                        hipStream_t stream) {
+  if (head_dim == 128 && kv_type == KV_BF16) return launch_mixed_t<128, 64, KV_BF16, 4>(pp, dp, total_q, stream);
+  if (head_dim == 256 && kv_type == KV_BF16) return launch_mixed_t<256, 32, KV_BF16, 2>(pp, dp, total_q, stream);
+  if (head_dim == 128 && kv_type == KV_FP8) return launch_mixed_t<128, 64, KV_FP8, 4>(pp, dp, total_q, stream);
+  if (head_dim == 256 && kv_type == KV_FP8) return launch_mixed_t<256, 32, KV_FP8, 2>(pp, dp, total_q, stream);
   return hipErrorInvalidValue;
 }
 

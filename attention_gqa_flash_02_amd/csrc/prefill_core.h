@@ -1,11 +1,13 @@
-// Tiled causal/non-causal varlen prefill for gfx950 on bf16 MFMA.
+// Tiled causal/non-causal prefill for gfx950 on bf16 MFMA, over contiguous or paged K/V.
 //
 // What it computes ("Attention kernels", section "FlashAttention"): Q, K and V
 // are cut into tiles; each workgroup keeps its query rows in registers,
 // streams K/V tiles through LDS, and per tile computes the scores, updates each
 // row's running maximum and exponential sum (rescaling what it has accumulated
 // when the maximum moves) and accumulates P V. Only O and one log-sum-exp per
-// row are written; the score matrix never leaves the chip.
+// row are written; the score matrix never leaves the chip. Causal masking is
+// bottom-right aligned: row i of a request with Lq new rows and Lk keys sees
+// keys j <= Lk - Lq + i (for self-attention Lq = Lk).
 //
 // Layout of the work:
 //   * a workgroup is 4 waves; each wave owns 32 query rows = 32 tokens of one
@@ -16,8 +18,8 @@
 //     columns, so every lane owns one query row and its softmax state lives in
 //     that lane (plus its partner lane 32 apart).
 //   * A-row i of a 32-key block loads key pi(i) = i with bits 2 and 3 swapped;
-//     then accumulator r of lane half h holds key 16*(r/8) + 8*h + r%8, and the
-//     8 k-slots a lane feeds to the P V MFMA are 8 consecutive keys: V^T is
+//     then accumulator r of lane half hh holds key 16*(r/8) + 8*hh + r%8, and
+//     the 8 k-slots a lane feeds to the P V MFMA are 8 consecutive keys: V^T is
 //     read from LDS with one 16-byte read per MFMA operand.
 //   * O^T += V^T P^T on 32x32x16 MFMA, P^T being the bf16-rounded S^T
 //     accumulator (no shuffle, no LDS round trip for P).
@@ -25,21 +27,45 @@
 //     strides are padded by 16 bytes so that the MFMA operand reads are free of
 //     bank conflicts. LDS is double-buffered: tile n+1 is fetched into
 //     registers while tile n is computed.
+//   * softmax state in the base-2 exponent domain (t = c * s, c = scale *
+//     log2 e): a reference maximum mc per row that only moves when a tile's
+//     maximum exceeds it by more than 2^8 (so the O rescale is skipped on
+//     almost every tile); the row sum is kept in fp32 (the log-sum-exp carries no
+//     bf16 rounding of P). Tiles crossing the causal diagonal or the end
+//     of the keys mask their scores and carry P as hi + lo bf16 parts (there a
+//     row sees few keys and the rounding of P would not average out).
+//   * K/V come from contiguous [tokens, Hkv, D] bf16 tensors or from a paged
+//     cache (K pages [Hkv][bs][D], V pages [Hkv][D][bs], bf16 or OCP e4m3fn
+//     codes dequantised to bf16 on the way into LDS; the per-head k_scale is
+//     folded into c and v_scale into the final normalisation).
 #pragma once
 
 #include "common.h"
 
 namespace attn {
 
+enum { KVSRC_CONTIG = 0, KVSRC_PAGED_BF16 = 1, KVSRC_PAGED_FP8 = 2 };
+
 struct PrefillParams {
-  const bf16* q;               // [T, Hq, D]
+  const bf16* q;               // [Tq, Hq, D]
+  bf16* out;                   // [Tq, Hq, D]
+  float* lse;                  // [Tq, Hq] or nullptr
+  const int32_t* cu_seqlens_q; // [B + 1]
+  // contiguous K/V (self-attention: request b owns rows cu_seqlens_q[b] .. of k and v)
   const bf16* k;               // [T, Hkv, D]
   const bf16* v;               // [T, Hkv, D]
-  const int32_t* cu_seqlens;   // [B + 1]
-  bf16* out;                   // [T, Hq, D]
-  float* lse;                  // [T, Hq] or nullptr
+  // paged K/V
+  const void* k_cache;         // [num_blocks, Hkv, bs, D]
+  const void* v_cache;         // [num_blocks, Hkv, D, bs]
+  const float* k_scale;        // [Hkv] (fp8) or nullptr
+  const float* v_scale;        // [Hkv] (fp8) or nullptr
+  const int32_t* block_table;  // [B, max_blocks]
+  const int32_t* seq_lens_k;   // [B] keys per request (its Lq new tokens are the last ones)
+  // tile list of a mixed batch: prefill tile t of the launch -> request, q-tile (see
+  // prefill_tile_of); nullptr for a plain grid (x = head group, y = request, z = q-tile)
+  const int32_t* tile_prefix;  // [B + 1] prefix sums of q-tiles per request on this path
   float scale;
-  int num_seqs, Hq, Hkv, g, hpw, causal, num_qtiles;
+  int num_seqs, Hq, Hkv, g, hpw, causal, num_qtiles, bs, max_blocks;
 };
 
 template <int D, int BN>
@@ -50,11 +76,6 @@ struct PrefillShape {
   static constexpr int V_ELEMS = D * VS;
   static constexpr int BUF = K_ELEMS + V_ELEMS;
   static constexpr int LDS_BYTES = 2 * BUF * 2;     // two buffers of bf16
-  static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
-  static constexpr int K_LOADS = BN * KCH / 256;    // K chunks per thread per tile
-  static constexpr int K_ROWS_PER_PASS = 256 / KCH;
-  static constexpr int VKG = BN / 4;                // 4-key groups per V tile
-  static_assert(VKG * (D / 8) == 256, "V staging assumes one 4x8 block per thread");
   static_assert(BN % 32 == 0, "key tiles are whole 32-key MFMA blocks");
 };
 
@@ -63,13 +84,173 @@ __device__ __forceinline__ int key_perm32(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
+// ---------------------------------------------------------------------------------------------
+// K/V tile loaders: fetch(n) issues the global loads of key tile n into registers, stage(dst)
+// writes them into one LDS buffer (K [BN][KS] row-major, V^T [D][VS]). Keys at or past Lk are
+// zero in both (their scores are masked, and zero V keeps NaN-carrying slots out of P V).
+// ---------------------------------------------------------------------------------------------
+
+// Contiguous bf16 K/V [T, Hkv, D]: K rows are copied, V is transposed 4 keys x 8 d at a time.
 template <int D, int BN>
-__device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* smem, int hgrp, int b,
-                                                  int qt) {
+struct ContigLoader {
+  static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+  static constexpr int K_LOADS = BN * KCH / 256;
+  static constexpr int K_ROWS_PER_PASS = 256 / KCH;
+  static constexpr int VKG = BN / 4;                // 4-key groups per V tile
+  static_assert(VKG * (D / 8) == 256, "V staging assumes one 4x8 block per thread");
+  u32x4 kreg[K_LOADS];
+  u32x4 vreg[4];
+  const bf16* kbase;
+  const bf16* vbase;
+  size_t stride;
+  int Lk, kch, krow0, vkg, vdc;
+
+  __device__ __forceinline__ void init(const PrefillParams& p, int b, int kvh, int Lk_) {
+    const int tid = threadIdx.x;
+    const int seq0 = p.cu_seqlens_q[b];
+    stride = (size_t)p.Hkv * D;
+    kbase = p.k + (size_t)seq0 * stride + (size_t)kvh * D;
+    vbase = p.v + (size_t)seq0 * stride + (size_t)kvh * D;
+    Lk = Lk_;
+    kch = tid % KCH;
+    krow0 = tid / KCH;
+    vkg = tid % VKG;
+    vdc = tid / VKG;
+  }
+  __device__ __forceinline__ void fetch(int n) {
+    const int n0 = n * BN;
+#pragma unroll
+    for (int it = 0; it < K_LOADS; ++it) {
+      const int key = n0 + it * K_ROWS_PER_PASS + krow0;
+      kreg[it] = (key < Lk) ? ld16(kbase + (size_t)key * stride + 8 * kch) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int key = n0 + 4 * vkg + s;
+      vreg[s] = (key < Lk) ? ld16(vbase + (size_t)key * stride + 8 * vdc) : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void stage(bf16* Ks, bf16* Vt) {
+    using S = PrefillShape<D, BN>;
+#pragma unroll
+    for (int it = 0; it < K_LOADS; ++it)
+      *reinterpret_cast<u32x4*>(Ks + (it * K_ROWS_PER_PASS + krow0) * S::KS + 8 * kch) = kreg[it];
+    // transpose the 4 keys x 8 d block: d-row 8*vdc + e gets keys 4*vkg .. 4*vkg+3
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
+      *reinterpret_cast<u32x2*>(Vt + (8 * vdc + 2 * w) * S::VS + 4 * vkg) = u32x2{lo01, lo23};
+      *reinterpret_cast<u32x2*>(Vt + (8 * vdc + 2 * w + 1) * S::VS + 4 * vkg) = u32x2{hi01, hi23};
+    }
+  }
+};
+
+// Paged cache (bf16 or fp8 codes). K: thread loads 16 bytes of one key row (8 bf16 / 16 fp8
+// values); V^T: 16 bytes of one d row of one page (8 bf16 / 16 fp8 consecutive tokens). Tokens
+// past Lk read the request's last page (a valid address) and are zeroed.
+template <int D, int BN, bool FP8>
+struct PagedLoader {
+  static constexpr int ELT = FP8 ? 1 : 2;
+  static constexpr int VPL = 16 / ELT;              // values per 16-byte load
+  static constexpr int K_CH = D / VPL;              // 16-byte loads per K row
+  static constexpr int K_LOADS = BN * K_CH / 256;
+  static constexpr int V_CH = BN / VPL;             // 16-byte loads per V^T d row of the tile
+  static constexpr int V_LOADS = D * V_CH / 256;
+  static_assert(K_LOADS >= 1 && V_LOADS >= 1 && BN * K_CH % 256 == 0 && D * V_CH % 256 == 0, "tile split");
+  u32x4 kreg[K_LOADS];
+  u32x4 vreg[V_LOADS];
+  const char* kc;
+  const char* vc;
+  const int32_t* table;
+  size_t block_stride;                              // bytes between consecutive blocks
+  int Lk, bs;
+
+  __device__ __forceinline__ void init(const PrefillParams& p, int b, int kvh, int Lk_) {
+    const size_t page = (size_t)p.bs * D * ELT;
+    kc = reinterpret_cast<const char*>(p.k_cache) + (size_t)kvh * page;
+    vc = reinterpret_cast<const char*>(p.v_cache) + (size_t)kvh * page;
+    block_stride = (size_t)p.Hkv * page;
+    table = p.block_table + (size_t)b * p.max_blocks;
+    Lk = Lk_;
+    bs = p.bs;
+  }
+  __device__ __forceinline__ void fetch(int n) {
+    const int tid = threadIdx.x;
+    const int n0 = n * BN;
+    const int last = Lk - 1;
+#pragma unroll
+    for (int it = 0; it < K_LOADS; ++it) {
+      const int idx = it * 256 + tid;
+      const int key = n0 + idx / K_CH, ch = idx % K_CH;
+      const int kk = min(key, last);
+      const char* row = kc + (size_t)table[kk / bs] * block_stride + (size_t)(kk % bs) * D * ELT;
+      kreg[it] = (key < Lk) ? ld16(row + 16 * ch) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int it = 0; it < V_LOADS; ++it) {
+      const int idx = it * 256 + tid;
+      const int d = idx / V_CH, t0 = n0 + VPL * (idx % V_CH);
+      const int tt = min(t0, last & ~(VPL - 1));          // a VPL-aligned run inside a valid page
+      const char* src = vc + (size_t)table[tt / bs] * block_stride + ((size_t)d * bs + tt % bs) * ELT;
+      u32x4 w = ld16(src);
+      if (t0 + VPL > Lk) {                          // zero the tokens past the end
+        const int valid = Lk - t0;                  // may be <= 0
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int first = e * (4 / ELT);          // first value index held by dword e
+          uint32_t keep = 0;
+#pragma unroll
+          for (int v = 0; v < 4 / ELT; ++v)
+            if (first + v < valid) keep |= (FP8 ? 0xFFu : 0xFFFFu) << (8 * ELT * v);
+          w[e] &= keep;
+        }
+      }
+      vreg[it] = w;
+    }
+  }
+  __device__ __forceinline__ void stage(bf16* Ks, bf16* Vt) {
+    using S = PrefillShape<D, BN>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < K_LOADS; ++it) {
+      const int idx = it * 256 + tid;
+      const int key = idx / K_CH, ch = idx % K_CH;
+      bf16* dst = Ks + key * S::KS + VPL * ch;
+      if constexpr (FP8) {
+        *reinterpret_cast<bf16x8*>(dst) = fp8x8_to_bf16x8(kreg[it][0], kreg[it][1]);
+        *reinterpret_cast<bf16x8*>(dst + 8) = fp8x8_to_bf16x8(kreg[it][2], kreg[it][3]);
+      } else {
+        *reinterpret_cast<u32x4*>(dst) = kreg[it];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < V_LOADS; ++it) {
+      const int idx = it * 256 + tid;
+      const int d = idx / V_CH, t = VPL * (idx % V_CH);
+      bf16* dst = Vt + d * S::VS + t;
+      if constexpr (FP8) {
+        *reinterpret_cast<bf16x8*>(dst) = fp8x8_to_bf16x8(vreg[it][0], vreg[it][1]);
+        *reinterpret_cast<bf16x8*>(dst + 8) = fp8x8_to_bf16x8(vreg[it][2], vreg[it][3]);
+      } else {
+        *reinterpret_cast<u32x4*>(dst) = vreg[it];
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------------------------
+// One workgroup: q-tile qt of request b for head group hgrp.
+// ---------------------------------------------------------------------------------------------
+template <int D, int BN, class Loader, bool PAGED>
+__device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* smem, int hgrp, int b, int qt) {
   using S = PrefillShape<D, BN>;
   constexpr int NKB = BN / 32;      // 32-key blocks per tile
   constexpr int NDB = D / 32;       // 32-wide d blocks of O^T
   constexpr int NKK = D / 16;       // k-steps of the QK MFMA
+  constexpr float kLazyRescale = 8.f;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -81,86 +262,57 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
   const int head = kvh * p.g + (hgrp % groups_per_kv) * p.hpw + (wave % p.hpw);
   const int nwt = 4 / p.hpw;
   const int TQ = 32 * nwt;
-  const int seq0 = p.cu_seqlens[b];
-  const int L = p.cu_seqlens[b + 1] - seq0;
+  const int q0 = p.cu_seqlens_q[b];
+  const int Lq = p.cu_seqlens_q[b + 1] - q0;
+  const int Lk = PAGED ? p.seq_lens_k[b] : Lq;
   const int t0 = qt * TQ;
-  if (t0 >= L) return;
-  const int tw = t0 + 32 * (wave / p.hpw);               // first token of this wave
-  const bool wave_active = tw < L;
-  const int kv_end = p.causal ? min(L, t0 + TQ) : L;     // keys any row of the workgroup sees
-  const int ntiles = (kv_end + BN - 1) / BN;
-  const int wave_kv_end = p.causal ? min(L, tw + 32) : L;
-  const float c = p.scale * kLog2e;
+  if (t0 >= Lq) return;
+  const int tw = t0 + 32 * (wave / p.hpw);               // first query row of this wave
+  const bool wave_active = tw < Lq;
+  const int shift = Lk - Lq;                             // row i sees keys <= shift + i (causal)
+  // keys any row of the workgroup / of this wave sees
+  const int kv_end = p.causal ? min(Lk, shift + min(Lq, t0 + TQ)) : Lk;
+  const int wave_kv_end = p.causal ? min(Lk, shift + min(Lq, tw + 32)) : Lk;
+  const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  float kscale = 1.f, vscale = 1.f;
+  if (PAGED && p.k_scale) { kscale = p.k_scale[kvh]; vscale = p.v_scale[kvh]; }
+  const float c = p.scale * kscale * kLog2e;
 
-  // ---- Q^T operands: lane (j, hh) holds Q[token tw + j][16*kk + 8*hh .. +7].
+  // ---- Q^T operands: lane (j, hh) holds Q[row tw + j][16*kk + 8*hh .. +7].
   bf16x8 qB[NKK];
-  const int qtok = tw + j;
-  if (qtok < L) {
-    const bf16* qrow = p.q + ((size_t)(seq0 + qtok) * p.Hq + head) * D;
+  const int qrow_i = tw + j;
+  if (qrow_i < Lq) {
+    const bf16* qrow = p.q + ((size_t)(q0 + qrow_i) * p.Hq + head) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qB[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * hh);
   } else {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qB[kk] = bf16x8{};
   }
+  // last key row j may see, and the first key at which some row of the wave stops seeing keys
+  const int lim = p.causal ? min(shift + qrow_i, Lk - 1) : (Lk - 1);
+  // first key that some row of the wave does not see (tiles reaching it need the mask)
+  const int wave_mask_from = p.causal ? max(0, shift + tw + 1) : Lk;
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  float m = kNegInf, l = 0.f;
+  float mc = kNegInf, l = 0.f;
 
-  // ---- staging registers
-  u32x4 kreg[S::K_LOADS];
-  u32x4 vreg[4];
-  const int kch = tid % S::KCH;
-  const int krow0 = tid / S::KCH;
-  const int vkg = tid % S::VKG;
-  const int vdc = tid / S::VKG;
-  const size_t kv_stride = (size_t)p.Hkv * D;
-  const bf16* kbase = p.k + (size_t)seq0 * kv_stride + (size_t)kvh * D;
-  const bf16* vbase = p.v + (size_t)seq0 * kv_stride + (size_t)kvh * D;
-
-  auto fetch = [&](int n) {
-    const int n0 = n * BN;
-#pragma unroll
-    for (int it = 0; it < S::K_LOADS; ++it) {
-      const int key = n0 + it * S::K_ROWS_PER_PASS + krow0;
-      kreg[it] = (key < L) ? ld16(kbase + (size_t)key * kv_stride + 8 * kch) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int key = n0 + 4 * vkg + s;
-      vreg[s] = (key < L) ? ld16(vbase + (size_t)key * kv_stride + 8 * vdc) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto stage = [&](int buf) {
-    bf16* Ks = smem + buf * S::BUF;
-    bf16* Vt = Ks + S::K_ELEMS;
-#pragma unroll
-    for (int it = 0; it < S::K_LOADS; ++it)
-      *reinterpret_cast<u32x4*>(Ks + (it * S::K_ROWS_PER_PASS + krow0) * S::KS + 8 * kch) = kreg[it];
-    // transpose the 4 keys x 8 d block: d-row 8*vdc + e gets keys 4*vkg .. 4*vkg+3
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
-      *reinterpret_cast<u32x2*>(Vt + (8 * vdc + 2 * w) * S::VS + 4 * vkg) = u32x2{lo01, lo23};
-      *reinterpret_cast<u32x2*>(Vt + (8 * vdc + 2 * w + 1) * S::VS + 4 * vkg) = u32x2{hi01, hi23};
-    }
-  };
-
-  fetch(0);
-  stage(0);
+  Loader ld;
+  ld.init(p, b, kvh, Lk);
+  if (ntiles > 0) {
+    ld.fetch(0);
+    ld.stage(smem, smem + S::K_ELEMS);
+  }
   __syncthreads();
   const int kperm = key_perm32(j);
 
   for (int n = 0; n < ntiles; ++n) {
     const int cur = n & 1;
-    if (n + 1 < ntiles) fetch(n + 1);
+    if (n + 1 < ntiles) ld.fetch(n + 1);
     const int n0 = n * BN;
     if (wave_active && n0 < wave_kv_end) {
       const bf16* Ks = smem + cur * S::BUF;
@@ -176,72 +328,99 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
         for (int kk = 0; kk < NKK; ++kk)
           st[kb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(krow + 16 * kk), qB[kk], st[kb]);
       }
-      // mask (only tiles that cross the diagonal or the sequence end)
-      const bool need_mask = (n0 + BN > L) || (p.causal && n0 + BN - 1 > tw);
-      if (need_mask) {
-        const int lim = p.causal ? min(qtok, L - 1) : (L - 1);
+      // tiles that cross the causal edge of some row of the wave or the end of the keys
+      const bool edge = (n0 + BN > Lk) || (n0 + BN - 1 >= wave_mask_from);
+      float tmax = kNegInf;
+      if (edge) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = n0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
-            st[kb][r] = (key <= lim) ? st[kb][r] : kNegInf;
+            st[kb][r] = (key <= lim) ? st[kb][r] * c : kNegInf;
           }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) st[kb] *= c;
       }
-      float mloc = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, st[kb][r]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-      const float m_new = fmaxf(m, mloc);
-      const float base = (m_new == kNegInf) ? 0.f : m_new * c;
-      const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m * c - base);
-      m = m_new;
-      // P in bf16 for the MFMA. On tiles that cross the diagonal or the sequence end the rows
-      // see few keys, so the rounding of P would not average out: there P is carried as
-      // hi + lo bf16 parts and multiplied into V twice.
-      bf16x8 pB[NKB][2], pL[NKB][2];
-      float psum = 0.f;
+        for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(st[kb][r], st[kb][r + 1]));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      // move the reference (and rescale what was accumulated) only where the tile maximum is
+      // more than kLazyRescale above it; a row's first visible tile always moves it
+      const bool move = tmax > mc + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float alpha = move ? ((mc == kNegInf) ? 0.f : fast_exp2(mc - tmax)) : 1.f;
+        mc = move ? tmax : mc;
+        l *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x8 pv, pl;
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const float e = fast_exp2(__builtin_fmaf(st[kb][8 * t + s], c, -base));
-            psum += e;
-            pv[s] = (bf16)e;
-            pl[s] = (bf16)(e - (float)pv[s]);
-          }
-          pB[kb][t] = pv;
-          pL[kb][t] = pl;
-        }
-      l = l * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        acc[db] *= alpha;
-        const bf16* vrow = Vt + (32 * db + j) * S::VS + 8 * hh;
+        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      }
+      const float base = (mc == kNegInf) ? 0.f : mc;
+      if (!edge) {
+        bf16x8 pB[NKB][2];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + 32 * kb + 16 * t);
-            acc[db] = mfma_32x32x16(va, pB[kb][t], acc[db]);
-            if (need_mask) acc[db] = mfma_32x32x16(va, pL[kb][t], acc[db]);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+              const float e = fast_exp2(st[kb][8 * t + s] - base);
+              l += e;
+              pB[kb][t][s] = (bf16)e;
+            }
           }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16* vrow = Vt + (32 * db + j) * S::VS + 8 * hh;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              acc[db] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(vrow + 32 * kb + 16 * t), pB[kb][t], acc[db]);
+        }
+      } else {
+        // edge tile: P as hi + lo bf16 parts, the sum in fp32
+        bf16x8 pB[NKB][2], pL[NKB][2];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+              const float e = fast_exp2(st[kb][8 * t + s] - base);
+              l += e;
+              pB[kb][t][s] = (bf16)e;
+              pL[kb][t][s] = (bf16)(e - (float)pB[kb][t][s]);
+            }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16* vrow = Vt + (32 * db + j) * S::VS + 8 * hh;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + 32 * kb + 16 * t);
+              acc[db] = mfma_32x32x16(va, pB[kb][t], acc[db]);
+              acc[db] = mfma_32x32x16(va, pL[kb][t], acc[db]);
+            }
+        }
       }
     }
-    if (n + 1 < ntiles) stage(cur ^ 1);
+    if (n + 1 < ntiles) {
+      bf16* nb = smem + (cur ^ 1) * S::BUF;
+      ld.stage(nb, nb + S::K_ELEMS);
+    }
     __syncthreads();
   }
 
   // ---- epilogue: O / l (bf16, round to nearest even) and the natural-log LSE
   const float l_row = l + __shfl_xor(l, 32, kWave);
-  if (wave_active && qtok < L) {
-    const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
-    bf16* orow = p.out + ((size_t)(seq0 + qtok) * p.Hq + head) * D;
+  if (wave_active && qrow_i < Lq) {
+    const float inv = (l_row > 0.f) ? vscale / l_row : 0.f;
+    bf16* orow = p.out + ((size_t)(q0 + qrow_i) * p.Hq + head) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -250,7 +429,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
         *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * rb + 4 * hh) = f32x4_to_bf16x4(o4);
       }
     if (p.lse && hh == 0)
-      p.lse[(size_t)(seq0 + qtok) * p.Hq + head] = (l_row > 0.f) ? kLn2 * (m * c + fast_log2(l_row)) : kNegInf;
+      p.lse[(size_t)(q0 + qrow_i) * p.Hq + head] = (l_row > 0.f) ? kLn2 * (mc + fast_log2(l_row)) : kNegInf;
   }
 }
 

@@ -107,3 +107,53 @@ def test_decode_group_sizes_and_edges(gpu, g):
         out, lse = _run_decode(case, splits)
         ref_o, ref_l = oracle_paged(case)
         compare(out, lse, ref_o, ref_l, label=f"edges g={g} splits={splits}")
+
+
+# ---------------------------------------------------------------------------------------------
+# Mixed varlen batch over a paged cache (prefill chunks over cached prefixes + decode tokens in
+# one call), bf16 and fp8 e4m3fn KV.
+# ---------------------------------------------------------------------------------------------
+
+def _run_varlen(case, splits=0):
+    out, lse = lib.attn_varlen_paged(case.q, case.k_cache, case.v_cache, case.block_table, case.cu_seqlens_q,
+                                     case.seq_lens_k, case.causal, case.scale, k_scale=case.k_scale,
+                                     v_scale=case.v_scale, num_splits=splits)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_varlen_c5_shrunk(gpu):
+    case = _to(synth.config_case("c5", shrink=16), gpu)   # 1 chunk of 128 over a prefix + 7 decodes
+    out, lse = _run_varlen(case)
+    ref_o, ref_l = oracle_paged(case)
+    compare(out, lse, ref_o, ref_l, max_abs=MAX_ABS_FP8, label="c5/16")
+
+
+@pytest.mark.parametrize("kv_format", ["bf16", "e4m3fn"])
+@pytest.mark.parametrize("d,bs", [(128, 16), (256, 16), (128, 64)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_mixed(gpu, kv_format, d, bs, causal):
+    # decode rows (q_len 1..4 with g = 4 stay on the decode path), prefill chunks over prefixes,
+    # a chunk with no prefix, a request with no new rows
+    q_lens = [1, 3, 37, 64, 0, 130, 1, 5]
+    kv_lens = [1, 300, 37, 64 + 500, 17, 130 + 33, 2000, 5]
+    gen = torch.Generator().manual_seed(70 + d + bs)
+    case = _to(synth.make_paged(70 + d + bs, kv_lens, q_lens, 8, 2, d, bs, kv_format=kv_format, causal=causal,
+                                lengths_drawn=gen), gpu)
+    for splits in (0, 3):
+        out, lse = _run_varlen(case, splits)
+        ref_o, ref_l = oracle_paged(case)
+        tol = MAX_ABS_FP8 if kv_format == "e4m3fn" else 1e-2
+        compare(out, lse, ref_o, ref_l, max_abs=tol,
+                label=f"mixed {kv_format} d={d} bs={bs} causal={causal} splits={splits}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2), (16, 1), (32, 2)])
+def test_varlen_group_sizes(gpu, hq, hkv):
+    q_lens = [2, 1, 40, 17]
+    kv_lens = [100, 64, 40 + 90, 17]
+    gen = torch.Generator().manual_seed(90 + hq)
+    case = _to(synth.make_paged(90 + hq, kv_lens, q_lens, hq, hkv, 128, 16, lengths_drawn=gen), gpu)
+    out, lse = _run_varlen(case)
+    ref_o, ref_l = oracle_paged(case)
+    compare(out, lse, ref_o, ref_l, label=f"varlen hq={hq} hkv={hkv}")
