@@ -5,8 +5,14 @@ namespace attn {
 
 // Varlen self-attention over contiguous K/V. Grid: (head groups, requests, q-tiles), q-tiles
 // walked heaviest (last) first.
+// Two workgroups per compute unit (two waves per SIMD, so one wave's softmax overlaps the
+// other's MFMAs) when the head dimension leaves room in the register file.
+template <int D>
+constexpr int prefill_waves_per_eu() { return D <= 128 ? 2 : 1; }
+
 template <int D, int BN>
-__global__ __launch_bounds__(256) void prefill_varlen_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D>(), prefill_waves_per_eu<D>())))
+void prefill_varlen_kernel(PrefillParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   prefill_tile_body<D, BN, ContigLoader<D, BN>, false>(p, reinterpret_cast<bf16*>(smem_raw), blockIdx.x,
                                                         blockIdx.y, p.num_qtiles - 1 - (int)blockIdx.z);
@@ -22,7 +28,8 @@ __device__ __forceinline__ int prefill_qtiles(const PrefillParams& p, int b, int
 // path's shares (memory-bound; dispatched first so that they run beside the prefill tiles), the
 // rest are prefill q-tiles (compute-bound), heaviest tile of each request first.
 template <int D, int BN, int KVT, int NU>
-__global__ __launch_bounds__(256) void varlen_mixed_kernel(PrefillParams pp, PagedParams dp, int n_dec,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D>(), prefill_waves_per_eu<D>())))
+void varlen_mixed_kernel(PrefillParams pp, PagedParams dp, int n_dec,
                                                            int combine_floats) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* lds = reinterpret_cast<float*>(smem_raw);
