@@ -72,7 +72,7 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v, con
   if (!q || !k || !v || !cu_seqlens || !out) return ATTN_ERR_NULL;
   if (num_seqs <= 0 || total_tokens < 0 || max_seqlen < 0 || max_seqlen > total_tokens ||
       num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-      (causal != 0 && causal != 1) || !std::isfinite(scale))
+      (causal != 0 && causal != 1) || !(std::isfinite(scale) && scale >= 0.f))
     return ATTN_ERR_SHAPE;
   if (head_dim != 128 && head_dim != 256) return ATTN_ERR_UNSUPPORTED;
   if ((long long)total_tokens * num_q_heads * head_dim > (long long)INT_MAX * 8) return ATTN_ERR_SHAPE;
@@ -149,7 +149,7 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
                                   out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                   num_blocks, max_blocks_per_seq, num_splits);
   if (st != ATTN_OK) return st;
-  if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
+  if (!(std::isfinite(scale) && scale >= 0.f)) return ATTN_ERR_SHAPE;
   const int g = num_q_heads / num_kv_heads;
   if (g > 16) return ATTN_ERR_UNSUPPORTED;
   const int S = attn_decode_num_splits(num_seqs, num_kv_heads, head_dim, kv_dtype, block_size,
@@ -203,7 +203,7 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
   if (st != ATTN_OK) return st;
   if (!cu_seqlens_q) return ATTN_ERR_NULL;
   if (total_q < 0 || max_q_len < 0 || max_q_len > total_q || (causal != 0 && causal != 1) ||
-      !std::isfinite(scale))
+      !(std::isfinite(scale) && scale >= 0.f))
     return ATTN_ERR_SHAPE;
   if ((long long)total_q * num_q_heads * head_dim > (long long)INT_MAX * 8) return ATTN_ERR_SHAPE;
   const int S = attn_decode_num_splits(num_seqs, num_kv_heads, head_dim, kv_dtype, block_size,

@@ -67,6 +67,14 @@ __device__ __forceinline__ float add_bf16x2(bf16x2 v, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(v, bf16x2{(bf16)1.0f, (bf16)1.0f}, acc, false);
 }
 
+// max(a, b, c) in one v_max3_f32.
+__device__ __forceinline__ float max3(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
+
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ bf16x2 cvt_pk_bf16(float a, float b) {
+  return bf16x2{(bf16)a, (bf16)b};
+}
+
 // 2^x on the VALU transcendental unit.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

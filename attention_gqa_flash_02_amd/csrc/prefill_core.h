@@ -119,15 +119,24 @@ struct ContigLoader {
   }
   __device__ __forceinline__ void fetch(int n) {
     const int n0 = n * BN;
+    const bf16* kp = kbase + (size_t)(n0 + krow0) * stride + 8 * kch;
+    const bf16* vp = vbase + (size_t)(n0 + 4 * vkg) * stride + 8 * vdc;
+    if (n0 + BN <= Lk) {                            // whole tile inside the keys: no bounds checks
+#pragma unroll
+      for (int it = 0; it < K_LOADS; ++it) kreg[it] = ld16(kp + (size_t)it * K_ROWS_PER_PASS * stride);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) vreg[s] = ld16(vp + (size_t)s * stride);
+      return;
+    }
 #pragma unroll
     for (int it = 0; it < K_LOADS; ++it) {
       const int key = n0 + it * K_ROWS_PER_PASS + krow0;
-      kreg[it] = (key < Lk) ? ld16(kbase + (size_t)key * stride + 8 * kch) : u32x4{0, 0, 0, 0};
+      kreg[it] = (key < Lk) ? ld16(kp + (size_t)it * K_ROWS_PER_PASS * stride) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int key = n0 + 4 * vkg + s;
-      vreg[s] = (key < Lk) ? ld16(vbase + (size_t)key * stride + 8 * vdc) : u32x4{0, 0, 0, 0};
+      vreg[s] = (key < Lk) ? ld16(vp + (size_t)s * stride) : u32x4{0, 0, 0, 0};
     }
   }
   __device__ __forceinline__ void stage(bf16* Ks, bf16* Vt) {
@@ -330,24 +339,23 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
       }
       // tiles that cross the causal edge of some row of the wave or the end of the keys
       const bool edge = (n0 + BN > Lk) || (n0 + BN - 1 >= wave_mask_from);
-      float tmax = kNegInf;
       if (edge) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = n0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
-            st[kb][r] = (key <= lim) ? st[kb][r] * c : kNegInf;
+            st[kb][r] = (key <= lim) ? st[kb][r] : kNegInf;
           }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) st[kb] *= c;
       }
+      // tile maximum of the raw scores (c >= 0, so it maps to the maximum of t = c * s)
+      float tmax = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(st[kb][r], st[kb][r + 1]));
+        for (int r = 0; r < 16; r += 2) tmax = max3(tmax, st[kb][r], st[kb][r + 1]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      tmax = (tmax == kNegInf) ? kNegInf : tmax * c;
       // move the reference (and rescale what was accumulated) only where the tile maximum is
       // more than kLazyRescale above it; a row's first visible tile always moves it
       const bool move = tmax > mc + kLazyRescale;
@@ -358,20 +366,23 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
       }
-      const float base = (mc == kNegInf) ? 0.f : mc;
+      const float nbase = (mc == kNegInf) ? 0.f : -mc;   // p = 2^(c * s - mc)
       if (!edge) {
         bf16x8 pB[NKB][2];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-              const float e = fast_exp2(st[kb][8 * t + s] - base);
-              l += e;
-              pB[kb][t][s] = (bf16)e;
+            for (int s = 0; s < 8; s += 2) {
+              const float e0 = fast_exp2(__builtin_fmaf(st[kb][8 * t + s], c, nbase));
+              const float e1 = fast_exp2(__builtin_fmaf(st[kb][8 * t + s + 1], c, nbase));
+              l += e0;
+              l += e1;
+              const bf16x2 pe = cvt_pk_bf16(e0, e1);
+              pB[kb][t][s] = pe[0];
+              pB[kb][t][s + 1] = pe[1];
             }
-          }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const bf16* vrow = Vt + (32 * db + j) * S::VS + 8 * hh;
@@ -382,7 +393,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
               acc[db] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(vrow + 32 * kb + 16 * t), pB[kb][t], acc[db]);
         }
       } else {
-        // edge tile: P as hi + lo bf16 parts, the sum in fp32
+        // edge tile: P as hi + lo bf16 parts
         bf16x8 pB[NKB][2], pL[NKB][2];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -390,7 +401,8 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
           for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-              const float e = fast_exp2(st[kb][8 * t + s] - base);
+              const float x = st[kb][8 * t + s];
+              const float e = (x == kNegInf) ? 0.f : fast_exp2(__builtin_fmaf(x, c, nbase));
               l += e;
               pB[kb][t][s] = (bf16)e;
               pL[kb][t][s] = (bf16)(e - (float)pB[kb][t][s]);

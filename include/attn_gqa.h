@@ -37,6 +37,7 @@
  *   - head_dim must be 128 or 256; num_q_heads must be a multiple of
  *     num_kv_heads; block_size must be 16, 32, 64, 128 or 256; paged calls
  *     take at most 16384 requests.
+ *   - scale (every call) must be finite and >= 0; otherwise ATTN_ERR_SHAPE.
  *   - stream is a hipStream_t (NULL = the default stream). Calls return once
  *     the work is enqueued; results are valid after the stream synchronises.
  *   - Argument validation is synchronous and happens before anything is
@@ -78,7 +79,7 @@ const char* attn_status_string(attn_status status);
  * and attends within itself (Lq = Lk = its length).
  *   q [total_tokens, num_q_heads, head_dim] bf16; k, v [total_tokens, num_kv_heads, head_dim] bf16
  *   cu_seqlens [num_seqs + 1] int32 (device), cu_seqlens[0] = 0, cu_seqlens[num_seqs] = total_tokens
- *   causal: 0 or 1; scale: score multiplier (e.g. 1/sqrt(head_dim))
+ *   causal: 0 or 1; scale: score multiplier, finite and >= 0 (e.g. 1/sqrt(head_dim))
  *   out [total_tokens, num_q_heads, head_dim] bf16 (round to nearest even)
  *   lse [total_tokens, num_q_heads] fp32, or NULL to skip it
  *   max_seqlen: an upper bound on every request's length (sizes the grid)

@@ -45,7 +45,7 @@ def _prefill(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(cu=None), 1), (dict(out=None), 1),
     (dict(nseq=0), 2), (dict(hq=6, hkv=4), 2), (dict(hkv=0), 2), (dict(total=-1), 2), (dict(maxlen=17), 2),
-    (dict(causal=2), 2), (dict(scale=float("nan")), 2),
+    (dict(causal=2), 2), (dict(scale=float("nan")), 2), (dict(scale=-0.5), 2),
     (dict(d=64), 3), (dict(d=192), 3),
 ])
 def test_prefill_validation(kw, code):
