@@ -21,6 +21,9 @@ constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// Word 3 of a raw buffer resource on gfx950 (32-bit data format; no swizzle, no stride): out of
+// range accesses (offset >= num_records) read zero.
+constexpr int kBufferFlags = 0x00020000;
 
 // ---- MFMA (matrix cores). Lane layouts, for lane l of the 64-lane wave:
 //   16x16xK: A[i][k] at lane (i = l%16), k-slots KPL*(l/16) .. +KPL-1 (KPL = K/4)

@@ -146,6 +146,11 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) qB[kk] = bf16x8{};
     }
+    // An empty asm redefines the Q registers: their loads are waited for here, once, so the
+    // chunk loop never waits on the memory counter for them (which would also wait for the
+    // chunk's own K/V loads issued after them).
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(qB[kk]));
   }
 
   // Running statistics of row j, in the base-2 exponent domain t = c * s: mc is a reference

@@ -91,6 +91,9 @@ __device__ __forceinline__ int key_perm32(int i) {
 // ---------------------------------------------------------------------------------------------
 
 // Contiguous bf16 K/V [T, Hkv, D]: K rows are copied, V is transposed 4 keys x 8 d at a time.
+// Loads are buffer loads: per tile a resource whose range ends at the request's last key (so
+// rows past the keys read as zero, with no branch), and per-thread byte offsets that stay fixed
+// for the whole loop (so no register written in the loop is a pending load's address).
 template <int D, int BN>
 struct ContigLoader {
   static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
@@ -100,44 +103,41 @@ struct ContigLoader {
   static_assert(VKG * (D / 8) == 256, "V staging assumes one 4x8 block per thread");
   u32x4 kreg[K_LOADS];
   u32x4 vreg[4];
-  const bf16* kbase;
-  const bf16* vbase;
-  size_t stride;
-  int Lk, kch, krow0, vkg, vdc;
+  const char* kbase;
+  const char* vbase;
+  long long row_bytes;                              // bytes between consecutive tokens
+  long long end_bytes;                              // bytes from the first row to the end of the last key
+  int koff[K_LOADS], voff[4];
+  int kch, krow0, vkg, vdc;
 
-  __device__ __forceinline__ void init(const PrefillParams& p, int b, int kvh, int Lk_) {
+  __device__ __forceinline__ void init(const PrefillParams& p, int b, int kvh, int Lk) {
     const int tid = threadIdx.x;
     const int seq0 = p.cu_seqlens_q[b];
-    stride = (size_t)p.Hkv * D;
-    kbase = p.k + (size_t)seq0 * stride + (size_t)kvh * D;
-    vbase = p.v + (size_t)seq0 * stride + (size_t)kvh * D;
-    Lk = Lk_;
+    const long long stride = (long long)p.Hkv * D;
+    kbase = reinterpret_cast<const char*>(p.k + (size_t)seq0 * stride + (size_t)kvh * D);
+    vbase = reinterpret_cast<const char*>(p.v + (size_t)seq0 * stride + (size_t)kvh * D);
+    row_bytes = stride * 2;
+    end_bytes = Lk > 0 ? (long long)(Lk - 1) * row_bytes + D * 2 : 0;
     kch = tid % KCH;
     krow0 = tid / KCH;
     vkg = tid % VKG;
     vdc = tid / VKG;
+#pragma unroll
+    for (int it = 0; it < K_LOADS; ++it) koff[it] = (int)((it * K_ROWS_PER_PASS + krow0) * row_bytes + 16 * kch);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) voff[s] = (int)((4 * vkg + s) * row_bytes + 16 * vdc);
   }
   __device__ __forceinline__ void fetch(int n) {
-    const int n0 = n * BN;
-    const bf16* kp = kbase + (size_t)(n0 + krow0) * stride + 8 * kch;
-    const bf16* vp = vbase + (size_t)(n0 + 4 * vkg) * stride + 8 * vdc;
-    if (n0 + BN <= Lk) {                            // whole tile inside the keys: no bounds checks
+    const long long t = (long long)n * BN * row_bytes;
+    long long left = end_bytes - t;
+    left = left < 0 ? 0 : (left > (long long)BN * row_bytes ? (long long)BN * row_bytes : left);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + t), 0, (int)left, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + t), 0, (int)left, kBufferFlags);
 #pragma unroll
-      for (int it = 0; it < K_LOADS; ++it) kreg[it] = ld16(kp + (size_t)it * K_ROWS_PER_PASS * stride);
+    for (int it = 0; it < K_LOADS; ++it)
+      kreg[it] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(kr, koff[it], 0, 0));
 #pragma unroll
-      for (int s = 0; s < 4; ++s) vreg[s] = ld16(vp + (size_t)s * stride);
-      return;
-    }
-#pragma unroll
-    for (int it = 0; it < K_LOADS; ++it) {
-      const int key = n0 + it * K_ROWS_PER_PASS + krow0;
-      kreg[it] = (key < Lk) ? ld16(kp + (size_t)it * K_ROWS_PER_PASS * stride) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int key = n0 + 4 * vkg + s;
-      vreg[s] = (key < Lk) ? ld16(vp + (size_t)s * stride) : u32x4{0, 0, 0, 0};
-    }
+    for (int s = 0; s < 4; ++s) vreg[s] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(vr, voff[s], 0, 0));
   }
   __device__ __forceinline__ void stage(bf16* Ks, bf16* Vt) {
     using S = PrefillShape<D, BN>;
@@ -159,7 +159,8 @@ struct ContigLoader {
 
 // Paged cache (bf16 or fp8 codes). K: thread loads 16 bytes of one key row (8 bf16 / 16 fp8
 // values); V^T: 16 bytes of one d row of one page (8 bf16 / 16 fp8 consecutive tokens). Tokens
-// past Lk read the request's last page (a valid address) and are zeroed.
+// past Lk read the request's last page (a valid address, so the loads are unconditional) and
+// are zeroed when the registers are written to LDS.
 template <int D, int BN, bool FP8>
 struct PagedLoader {
   static constexpr int ELT = FP8 ? 1 : 2;
@@ -186,9 +187,11 @@ struct PagedLoader {
     Lk = Lk_;
     bs = p.bs;
   }
+  int tile0;
   __device__ __forceinline__ void fetch(int n) {
     const int tid = threadIdx.x;
     const int n0 = n * BN;
+    tile0 = n0;
     const int last = Lk - 1;
 #pragma unroll
     for (int it = 0; it < K_LOADS; ++it) {
@@ -196,7 +199,7 @@ struct PagedLoader {
       const int key = n0 + idx / K_CH, ch = idx % K_CH;
       const int kk = min(key, last);
       const char* row = kc + (size_t)table[kk / bs] * block_stride + (size_t)(kk % bs) * D * ELT;
-      kreg[it] = (key < Lk) ? ld16(row + 16 * ch) : u32x4{0, 0, 0, 0};
+      kreg[it] = ld16(row + 16 * ch);                 // rows past the keys are zeroed in stage
     }
 #pragma unroll
     for (int it = 0; it < V_LOADS; ++it) {
@@ -205,8 +208,20 @@ struct PagedLoader {
       const int tt = min(t0, last & ~(VPL - 1));          // a VPL-aligned run inside a valid page
       const char* src = vc + (size_t)table[tt / bs] * block_stride + ((size_t)d * bs + tt % bs) * ELT;
       u32x4 w = ld16(src);
-      if (t0 + VPL > Lk) {                          // zero the tokens past the end
-        const int valid = Lk - t0;                  // may be <= 0
+      vreg[it] = w;
+    }
+  }
+  __device__ __forceinline__ void stage(bf16* Ks, bf16* Vt) {
+    using S = PrefillShape<D, BN>;
+    const int tid = threadIdx.x;
+    if (tile0 + BN > Lk) {                          // the last tile: zero keys past the end
+#pragma unroll
+      for (int it = 0; it < K_LOADS; ++it)
+        if (tile0 + (it * 256 + tid) / K_CH >= Lk) kreg[it] = u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int it = 0; it < V_LOADS; ++it) {
+        const int t0 = tile0 + VPL * ((it * 256 + tid) % V_CH);
+        const int valid = Lk - t0;                  // values of this run that exist (may be <= 0)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int first = e * (4 / ELT);          // first value index held by dword e
@@ -214,15 +229,10 @@ struct PagedLoader {
 #pragma unroll
           for (int v = 0; v < 4 / ELT; ++v)
             if (first + v < valid) keep |= (FP8 ? 0xFFu : 0xFFFFu) << (8 * ELT * v);
-          w[e] &= keep;
+          vreg[it][e] &= keep;
         }
       }
-      vreg[it] = w;
     }
-  }
-  __device__ __forceinline__ void stage(bf16* Ks, bf16* Vt) {
-    using S = PrefillShape<D, BN>;
-    const int tid = threadIdx.x;
 #pragma unroll
     for (int it = 0; it < K_LOADS; ++it) {
       const int idx = it * 256 + tid;
@@ -298,6 +308,11 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qB[kk] = bf16x8{};
   }
+  // An empty asm redefines the Q registers: the loads are waited for here, once, and the loop
+  // never sees them as outstanding (it would otherwise wait on the memory counter before each
+  // QK MFMA, i.e. on the next tile's prefetch).
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qB[kk]));
   // last key row j may see, and the first key at which some row of the wave stops seeing keys
   const int lim = p.causal ? min(shift + qrow_i, Lk - 1) : (Lk - 1);
   // first key that some row of the wave does not see (tiles reaching it need the mask)
