@@ -2,20 +2,24 @@
 
 A step is one call of the paged GQA decode on the batch-32 workload (32 query /
 8 KV heads, head dim 128, bf16 KV in 16-token blocks with shuffled pages,
-lengths uniform in [1024, 8192]): split-KV partitions + LSE merge in one
-launch. `value` is KV bytes read per second over the timed steps (inputs
-resident in HBM; the KV cache is rotated over copies so that no step finds it
-in the 256 MB last-level cache). The same run also times the causal varlen
-prefill (4 x 8192 tokens, 32/8 heads, D 128) and the long-context split-KV
-decode (2 x 131072 tokens, 32/2 heads, 64-token blocks), reports each against
-its roofline, checks sampled outputs against the fp64 oracle, and times the
-oracle itself on the host cores (cpu_baseline).
+lengths uniform in [1024, 8192]): the partition kernel (balanced split-KV
+shares) plus the LSE merge kernel. `value` is KV bytes read per second over the
+timed steps (inputs resident in HBM; the KV cache is rotated over copies so
+that no step finds it in the 256 MB last-level cache). The same run also times
+the causal varlen prefill (4 x 8192 tokens, 32/8 heads, D 128), the
+long-context split-KV decode (2 x 131072 tokens, 32/2 heads, 64-token blocks)
+and the mixed fp8 batch (8 prefill chunks of 2048 over cached prefixes + 120
+decodes, 16/4 heads, D 256), reports each against its roofline, checks sampled
+outputs against the fp64 oracle, and times the oracle itself on the host cores
+(cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c2|c3|c4|c5]
+                       [--no-cpu-baseline] [--quick]
 Prints one JSON line.
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -28,6 +32,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 4096 flop/clk x 2.4 GHz)
+CSRC = os.path.join(ROOT, "attention_gqa_flash_02_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def log(msg):
@@ -40,23 +46,48 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--splits", type=int, default=0, help="decode partitions (0 = library choice)")
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5"], default=None,
+                    help="time one workload only (for profiling); the JSON line still names c2's metric")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="time only the headline decode workload")
     ap.add_argument("--quick", action="store_true", help="skip the parity samples")
     return ap.parse_args()
 
 
+def sources_digest(names):
+    """sha256 over the named kernel sources: traffic figures are only valid for the code they were
+    measured on."""
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key, sources):
+    """HBM bytes per call from profiles/traffic.json (FETCH_SIZE + WRITE_SIZE of the kernels of one
+    call, scaled by a copy-kernel calibration), or None when absent or measured on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entry = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("sources_sha256_16") != sources_digest(sources):
+        return None
+    return entry.get("hbm_bytes_per_call")
+
+
 def time_steps(fns, steps, warmup):
     """Run fns round-robin: warmup untimed, then `steps` timed between synchronisations.
-    Returns (wall ms per step, per-call event durations in ms)."""
+    Returns (wall ms per step, per-call event durations in ms) -- events on the current stream,
+    which is the stream the library launches on."""
     import torch
     n = len(fns)
     for i in range(warmup):
         fns[i % n]()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -69,12 +100,12 @@ def time_steps(fns, steps, warmup):
     return wall, durs
 
 
-def rotate_paged(case, copies):
-    """Independent copies of the KV cache (same contents, different addresses)."""
-    out = [(case.k_cache, case.v_cache)]
-    for _ in range(copies - 1):
-        out.append((case.k_cache.clone(), case.v_cache.clone()))
-    return out
+def to_device(case, dev):
+    import torch
+    for k, v in list(vars(case).items()):
+        if isinstance(v, torch.Tensor):
+            setattr(case, k, v.to(dev))
+    return case
 
 
 def decode_section(lib, case, splits, steps, warmup, label):
@@ -83,12 +114,13 @@ def decode_section(lib, case, splits, steps, warmup, label):
     kv_bytes = workmodel.kv_bytes(case.kv_lens, case.num_kv_heads, case.head_dim,
                                   2 if case.kv_format == "bf16" else 1)
     copies = max(2, math.ceil(3 * 256e6 / kv_bytes) + 1)
-    caches = rotate_paged(case, copies)
+    caches = [(case.k_cache, case.v_cache)] + [(case.k_cache.clone(), case.v_cache.clone())
+                                               for _ in range(copies - 1)]
     b, hq, d = case.q.shape
     hkv, bs = case.num_kv_heads, case.block_size
     maxblk = case.block_table.shape[1]
     s = lib.attn_decode_num_splits(b, hkv, d, 0 if case.kv_format == "bf16" else 1, bs, maxblk, splits)
-    ws = torch.zeros(max(1, lib.attn_decode_workspace_bytes(b, hkv, d, s)), dtype=torch.uint8, device=case.q.device)
+    ws = torch.empty(max(1, lib.attn_decode_workspace_bytes(b, hkv, d, s)), dtype=torch.uint8, device=case.q.device)
     out = torch.empty_like(case.q)
     lse = torch.empty((b, hq), dtype=torch.float32, device=case.q.device)
 
@@ -98,7 +130,7 @@ def decode_section(lib, case, splits, steps, warmup, label):
                                              num_splits=s, workspace=ws)
     wall, durs = time_steps([make(kc, vc) for kc, vc in caches], steps, warmup)
     kern = statistics.mean(durs)
-    log(f"[bench] {label}: splits={s} copies={copies} wall/step={wall:.4f} ms kernel mean={kern:.4f} "
+    log(f"[bench] {label}: partitions={s} copies={copies} wall/step={wall:.4f} ms call mean={kern:.4f} "
         f"median={statistics.median(durs):.4f} min={min(durs):.4f} ms -> {kv_bytes / kern / 1e6:.1f} GB/s")
     return {"kv_bytes": kv_bytes, "splits": s, "wall_ms": wall, "kernel_ms_mean": kern,
             "kernel_ms_median": statistics.median(durs), "kernel_ms_min": min(durs), "out": out, "lse": lse}
@@ -121,37 +153,69 @@ def prefill_section(lib, case, steps, warmup):
             "lse": lse}
 
 
-def sampled_parity_paged(case, out, lse, units):
+def mixed_section(lib, case, steps, warmup):
+    import torch
+    from attention_gqa_flash_02_amd import workmodel
+    pre = [(ql, kl) for ql, kl in zip(case.q_lens, case.kv_lens) if ql * (case.num_q_heads // case.num_kv_heads) > 16]
+    dec = [kl for ql, kl in zip(case.q_lens, case.kv_lens) if 0 < ql * (case.num_q_heads // case.num_kv_heads) <= 16]
+    flops = workmodel.prefill_flops([a for a, _ in pre], [b for _, b in pre], case.num_q_heads, case.head_dim, True)
+    dec_bytes = workmodel.kv_bytes(dec, case.num_kv_heads, case.head_dim, 1)
+    pre_kv_bytes = workmodel.kv_bytes([b for _, b in pre], case.num_kv_heads, case.head_dim, 1)
+    b = case.seq_lens_k.numel()
+    s = lib.attn_decode_num_splits(b, case.num_kv_heads, case.head_dim, 1, case.block_size,
+                                   case.block_table.shape[1], 0)
+    ws = torch.empty(lib.attn_varlen_workspace_bytes(b, case.num_kv_heads, case.head_dim, s), dtype=torch.uint8,
+                     device=case.q.device)
+    out = torch.empty_like(case.q)
+    lse = torch.empty((case.q.shape[0], case.q.shape[1]), dtype=torch.float32, device=case.q.device)
+    max_q = max(case.q_lens)
+
+    def call():
+        lib.attn_varlen_paged(case.q, case.k_cache, case.v_cache, case.block_table, case.cu_seqlens_q,
+                              case.seq_lens_k, True, case.scale, k_scale=case.k_scale, v_scale=case.v_scale,
+                              out=out, lse=lse, max_q_len=max_q, num_splits=s, workspace=ws)
+    wall, durs = time_steps([call], steps, warmup)
+    kern = statistics.mean(durs)
+    t_star = max(flops / (MFMA_BF16_PEAK_TFS * 1e9), (dec_bytes + pre_kv_bytes) / (HBM_PEAK_GBS * 1e6))
+    log(f"[bench] mixed c5: call mean={kern:.4f} ms -> prefill part {flops / kern / 1e9:.1f} TFLOP/s, decode part "
+        f"{dec_bytes / kern / 1e6:.1f} GB/s; roofline lower bound {t_star:.4f} ms ({t_star / kern:.3f})")
+    return {"flops": flops, "decode_kv_bytes": dec_bytes, "prefill_kv_bytes": pre_kv_bytes, "ms": kern,
+            "wall_ms": wall, "t_star_ms": t_star, "out": out, "lse": lse}
+
+
+def parity_stats(out, lse, ref_o, ref_l):
     import numpy as np
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from helpers import oracle_paged, bf16_np
-    ref_o, ref_l = oracle_paged(case, units=units)
+    from helpers import bf16_np
     o = bf16_np(out)
     m = ~np.isnan(ref_o)
     err = np.abs(o[m] - ref_o[m])
     l = lse.cpu().numpy().astype(np.float64)
     lm = ~np.isnan(ref_l)
-    return {"units": len(units), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
-            "lse_max_abs": float(np.abs(l[lm] - ref_l[lm]).max())}
+    return {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+            "lse_max_abs": float(np.abs(l[lm] - ref_l[lm]).max()), "max_ref": float(np.abs(ref_o[m]).max())}
+
+
+def sampled_parity_paged(case, out, lse, units):
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import oracle_paged
+    ref_o, ref_l = oracle_paged(case, units=units)
+    r = parity_stats(out, lse, ref_o, ref_l)
+    r["units"] = len(units)
+    return r
 
 
 def sampled_parity_prefill(case, out, lse, units):
-    import numpy as np
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from helpers import oracle_prefill, bf16_np
+    from helpers import oracle_prefill
     ref_o, ref_l = oracle_prefill(case, units=units)
-    o = bf16_np(out)
-    m = ~np.isnan(ref_o)
-    err = np.abs(o[m] - ref_o[m])
-    l = lse.cpu().numpy().astype(np.float64)
-    lm = ~np.isnan(ref_l)
-    return {"units": len(units), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
-            "lse_max_abs": float(np.abs(l[lm] - ref_l[lm]).max())}
+    r = parity_stats(out, lse, ref_o, ref_l)
+    r["units"] = len(units)
+    return r
 
 
 def cpu_baseline_decode(case):
-    """The fp64 oracle over the whole decode workload on the host cores."""
-    import numpy as np
+    """The fp64 oracle over the whole batch-32 decode workload on the host cores."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from helpers import bf16_np, cache_np
     from oracle import parallel
@@ -183,86 +247,125 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] device: {torch.cuda.get_device_name(dev)}; library {lib.library_path()}")
+    run = (lambda name: a.only is None or a.only == name)
+    extra = {}
 
     # ---- headline: paged GQA decode, batch 32 (generated on the host, copied to the GPU)
-    t = time.perf_counter()
-    c2 = synth.config_case("c2")
-    c2_host = c2
-    c2 = synth.PagedCase(**{k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in vars(c2).items()})
-    log(f"[bench] decode workload ready in {time.perf_counter() - t:.1f} s: sum(len)={sum(c2.kv_lens)}")
-    dec = decode_section(lib, c2, a.splits, a.steps, a.warmup, "decode c2")
-    result_extra = {}
-    if not a.quick:
-        rng = np.random.default_rng(0)
-        units = [(int(b), int(h)) for b, h in zip(rng.integers(0, 32, 64), rng.integers(0, 32, 64))]
-        par = sampled_parity_paged(c2_host, dec["out"], dec["lse"], units)
-        log(f"[bench] decode c2 parity on {par['units']} sampled (request, head) units: {par}")
-        result_extra["decode_parity_sample"] = par
+    dec = None
+    c2_host = None
+    if run("c2"):
+        t = time.perf_counter()
+        c2_host = synth.config_case("c2")
+        c2 = to_device(synth.config_case("c2"), dev)
+        log(f"[bench] decode workload ready in {time.perf_counter() - t:.1f} s: sum(len)={sum(c2.kv_lens)}")
+        dec = decode_section(lib, c2, a.splits, a.steps, a.warmup, "decode c2")
+        if not a.quick:
+            rng = np.random.default_rng(0)
+            units = [(int(b), int(h)) for b, h in zip(rng.integers(0, 32, 64), rng.integers(0, 32, 64))]
+            par = sampled_parity_paged(c2_host, dec["out"], dec["lse"], units)
+            log(f"[bench] decode c2 parity on {par['units']} sampled (request, head) units: {par}")
+            extra["decode_parity_sample"] = par
+        del c2
+        torch.cuda.empty_cache()
 
-    if not a.no_extra:
-        # ---- causal varlen prefill 4 x 8192 (generated on the GPU)
+    if run("c3"):
         c3 = synth.config_case("c3", device=dev)
         pre = prefill_section(lib, c3, max(5, a.steps // 5), max(2, a.warmup // 2))
         tf = pre["flops"] / pre["kernel_ms_mean"] / 1e9
-        result_extra["prefill_c3"] = {
+        extra["prefill_c3"] = {
             "workload": "causal varlen prefill, 4 x 8192 tokens, 32/8 heads, D 128, bf16, out + LSE",
             "tflops": tf, "ms": pre["kernel_ms_mean"], "wall_ms": pre["wall_ms"],
             "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": tf / MFMA_BF16_PEAK_TFS, "traffic": None},
+                         "frac": tf / MFMA_BF16_PEAK_TFS,
+                         "traffic": measured_traffic("prefill_c3", ["common.h", "prefill_core.h", "prefill.hip"])},
             "algorithmic_flops": pre["flops"]}
         if not a.quick:
             units = [(0, 0), (1, 7), (2, 19), (3, 31)]
             par = sampled_parity_prefill(c3, pre["out"], pre["lse"], units)
             log(f"[bench] prefill parity on {units}: {par}")
-            result_extra["prefill_c3"]["parity_sample"] = par
+            extra["prefill_c3"]["parity_sample"] = par
         del c3, pre
         torch.cuda.empty_cache()
 
-        # ---- long-context split-KV decode 2 x 131072 (generated on the GPU)
+    if run("c4"):
         c4 = synth.config_case("c4", device=dev)
         best = None
-        for s in (16, 32, 64, 128, 256):
-            r = decode_section(lib, c4, s, a.steps, a.warmup, f"decode c4 splits={s}")
+        for s in (0, 512):
+            r = decode_section(lib, c4, s, a.steps, a.warmup, f"decode c4 partitions={s or 'auto'}")
             if best is None or r["kernel_ms_mean"] < best["kernel_ms_mean"]:
                 best = r
         gbs = best["kv_bytes"] / best["kernel_ms_mean"] / 1e6
-        result_extra["decode_c4"] = {
+        extra["decode_c4"] = {
             "workload": "split-KV decode, 2 x 131072 tokens, 32/2 heads, D 128, bf16 KV, 64-token blocks",
-            "gbs": gbs, "splits": best["splits"], "ms": best["kernel_ms_mean"],
+            "gbs": gbs, "partitions": best["splits"], "ms": best["kernel_ms_mean"],
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+        if not a.quick:
+            units = [(0, 0), (1, 17), (0, 31)]
+            par = sampled_parity_paged(c4, best["out"], best["lse"], units)
+            log(f"[bench] decode c4 parity on {units}: {par}")
+            extra["decode_c4"]["parity_sample"] = par
         del c4
         torch.cuda.empty_cache()
 
+    if run("c5"):
+        t = time.perf_counter()
+        c5 = synth.config_case("c5", device=dev)
+        log(f"[bench] mixed workload ready in {time.perf_counter() - t:.1f} s: q rows {c5.q.shape[0]}, "
+            f"keys {sum(c5.kv_lens)}")
+        mx = mixed_section(lib, c5, max(5, a.steps // 5), max(2, a.warmup // 2))
+        extra["mixed_c5"] = {
+            "workload": "one call: 8 prefill chunks of 2048 over cached prefixes U[0, 32768] + 120 decodes with "
+                        "contexts U[512, 32768], 16/4 heads, D 256, fp8 e4m3fn KV with per-head scales",
+            "ms": mx["ms"], "prefill_tflops": mx["flops"] / mx["ms"] / 1e9,
+            "decode_gbs": mx["decode_kv_bytes"] / mx["ms"] / 1e6,
+            "algorithmic_flops": mx["flops"], "decode_kv_bytes": mx["decode_kv_bytes"],
+            "prefill_kv_bytes": mx["prefill_kv_bytes"],
+            "roofline": {"bound": "mfma", "lower_bound_ms": mx["t_star_ms"], "frac": mx["t_star_ms"] / mx["ms"]}}
+        if not a.quick:
+            n_pre = sum(1 for ql in c5.q_lens if ql > 1)
+            units = [(0, 0), (n_pre - 1, 15), (n_pre, 3), (n_pre + 50, 9), (len(c5.q_lens) - 1, 12)]
+            par = sampled_parity_paged(c5, mx["out"], mx["lse"], units)
+            log(f"[bench] mixed c5 parity on {units}: {par}")
+            extra["mixed_c5"]["parity_sample"] = par
+        del c5, mx
+        torch.cuda.empty_cache()
+
     cpu = None
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and run("c2"):
         cpu = cpu_baseline_decode(c2_host)
         log(f"[bench] cpu baseline: {cpu}")
 
-    achieved = dec["kv_bytes"] / dec["kernel_ms_mean"] / 1e6
-    value = dec["kv_bytes"] / dec["wall_ms"] / 1e6
     line = {
         "metric": "decode attn KV GB/s (% HBM peak)",
-        "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(dec["wall_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled pages)",
-        "config": {"workload": "paged GQA decode: batch 32, 32 q / 8 kv heads, head_dim 128, bf16 KV in "
-                               "16-token blocks, lengths U[1024, 8192]",
-                   "global_batch": 32, "seq_len": "U[1024, 8192]", "num_splits": dec["splits"],
-                   "kv_bytes": dec["kv_bytes"], "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": cpu,
-        "extra": result_extra,
+        "extra": extra,
     }
+    if dec is not None:
+        achieved = dec["kv_bytes"] / dec["kernel_ms_mean"] / 1e6
+        line.update({
+            "value": round(dec["kv_bytes"] / dec["wall_ms"] / 1e6, 2),
+            "ms_per_step": round(dec["wall_ms"], 5),
+            "config": {"workload": "paged GQA decode: batch 32, 32 q / 8 kv heads, head_dim 128, bf16 KV in "
+                                   "16-token blocks, lengths U[1024, 8192]",
+                       "global_batch": 32, "seq_len": "U[1024, 8192]", "num_partitions": dec["splits"],
+                       "kv_bytes": dec["kv_bytes"], "parallelism": "single GPU"},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_paged_c2", ["common.h", "decode_core.h", "decode.hip"])},
+        })
+    else:
+        line.update({"value": None, "ms_per_step": None,
+                     "config": {"workload": f"only {a.only} timed (see extra)"}, "roofline": None})
     print(json.dumps(line), flush=True)
 
 
