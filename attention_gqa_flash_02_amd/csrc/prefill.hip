@@ -77,7 +77,7 @@ static hipError_t launch_prefill_t(const PrefillParams& p, int max_seqlen, hipSt
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, hipStream_t stream) {
   if (head_dim == 128) return launch_prefill_t<128, 64>(p, max_seqlen, stream);
-  if (head_dim == 256) return launch_prefill_t<256, 32>(p, max_seqlen, stream);
+  if (head_dim == 256) return launch_prefill_t<256, 64>(p, max_seqlen, stream);
   return hipErrorInvalidValue;
 }
 
@@ -108,9 +108,9 @@ static hipError_t launch_mixed_t(const PrefillParams& pp, const PagedParams& dp,
 hipError_t launch_mixed(const PrefillParams& pp, const PagedParams& dp, int head_dim, int kv_type, int total_q,
                         hipStream_t stream) {
   if (head_dim == 128 && kv_type == KV_BF16) return launch_mixed_t<128, 64, KV_BF16, 4>(pp, dp, total_q, stream);
-  if (head_dim == 256 && kv_type == KV_BF16) return launch_mixed_t<256, 32, KV_BF16, 2>(pp, dp, total_q, stream);
+  if (head_dim == 256 && kv_type == KV_BF16) return launch_mixed_t<256, 64, KV_BF16, 2>(pp, dp, total_q, stream);
   if (head_dim == 128 && kv_type == KV_FP8) return launch_mixed_t<128, 64, KV_FP8, 4>(pp, dp, total_q, stream);
-  if (head_dim == 256 && kv_type == KV_FP8) return launch_mixed_t<256, 32, KV_FP8, 2>(pp, dp, total_q, stream);
+  if (head_dim == 256 && kv_type == KV_FP8) return launch_mixed_t<256, 64, KV_FP8, 2>(pp, dp, total_q, stream);
   return hipErrorInvalidValue;
 }
 

@@ -100,14 +100,15 @@ struct ContigLoader {
   static constexpr int K_LOADS = BN * KCH / 256;
   static constexpr int K_ROWS_PER_PASS = 256 / KCH;
   static constexpr int VKG = BN / 4;                // 4-key groups per V tile
-  static_assert(VKG * (D / 8) == 256, "V staging assumes one 4x8 block per thread");
+  static constexpr int VB = VKG * (D / 8) / 256;    // 4-key x 8-d blocks of V per thread
+  static_assert(VB >= 1 && VKG * (D / 8) % 256 == 0, "V staging splits into whole 4x8 blocks");
   u32x4 kreg[K_LOADS];
-  u32x4 vreg[4];
+  u32x4 vreg[4 * VB];
   const char* kbase;
   const char* vbase;
   long long row_bytes;                              // bytes between consecutive tokens
   long long end_bytes;                              // bytes from the first row to the end of the last key
-  int koff[K_LOADS], voff[4];
+  int koff[K_LOADS], voff[4 * VB];
   int kch, krow0, vkg, vdc;
 
   __device__ __forceinline__ void init(const PrefillParams& p, int b, int kvh, int Lk) {
@@ -125,7 +126,10 @@ struct ContigLoader {
 #pragma unroll
     for (int it = 0; it < K_LOADS; ++it) koff[it] = (int)((it * K_ROWS_PER_PASS + krow0) * row_bytes + 16 * kch);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) voff[s] = (int)((4 * vkg + s) * row_bytes + 16 * vdc);
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        voff[4 * vb + s] = (int)((4 * vkg + s) * row_bytes + 16 * (vdc + vb * (256 / VKG)));
   }
   __device__ __forceinline__ void fetch(int n) {
     const long long t = (long long)n * BN * row_bytes;
@@ -137,22 +141,27 @@ struct ContigLoader {
     for (int it = 0; it < K_LOADS; ++it)
       kreg[it] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(kr, koff[it], 0, 0));
 #pragma unroll
-    for (int s = 0; s < 4; ++s) vreg[s] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(vr, voff[s], 0, 0));
+    for (int s = 0; s < 4 * VB; ++s) vreg[s] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(vr, voff[s], 0, 0));
   }
   __device__ __forceinline__ void stage(bf16* Ks, bf16* Vt) {
     using S = PrefillShape<D, BN>;
 #pragma unroll
     for (int it = 0; it < K_LOADS; ++it)
       *reinterpret_cast<u32x4*>(Ks + (it * K_ROWS_PER_PASS + krow0) * S::KS + 8 * kch) = kreg[it];
-    // transpose the 4 keys x 8 d block: d-row 8*vdc + e gets keys 4*vkg .. 4*vkg+3
+    // transpose each 4 keys x 8 d block: d-row 8*dc + e gets keys 4*vkg .. 4*vkg+3
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
-      *reinterpret_cast<u32x2*>(Vt + (8 * vdc + 2 * w) * S::VS + 4 * vkg) = u32x2{lo01, lo23};
-      *reinterpret_cast<u32x2*>(Vt + (8 * vdc + 2 * w + 1) * S::VS + 4 * vkg) = u32x2{hi01, hi23};
+    for (int vb = 0; vb < VB; ++vb) {
+      const int dc = vdc + vb * (256 / VKG);
+      const u32x4* v = vreg + 4 * vb;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo01 = __builtin_amdgcn_perm(v[1][w], v[0][w], 0x05040100u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(v[3][w], v[2][w], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(v[1][w], v[0][w], 0x07060302u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(v[3][w], v[2][w], 0x07060302u);
+        *reinterpret_cast<u32x2*>(Vt + (8 * dc + 2 * w) * S::VS + 4 * vkg) = u32x2{lo01, lo23};
+        *reinterpret_cast<u32x2*>(Vt + (8 * dc + 2 * w + 1) * S::VS + 4 * vkg) = u32x2{hi01, hi23};
+      }
     }
   }
 };
@@ -186,9 +195,25 @@ struct PagedLoader {
     table = p.block_table + (size_t)b * p.max_blocks;
     Lk = Lk_;
     bs = p.bs;
+    if (Lk > 0) load_table(0);
   }
+  // Block-table entries are loaded one tile ahead of the K/V loads that use them, so a fetch
+  // never waits on a table load.
+  int kphys[K_LOADS], vphys[V_LOADS];
   int tile0;
-  __device__ __forceinline__ void fetch(int n) {
+  __device__ __forceinline__ void load_table(int n) {
+    const int tid = threadIdx.x;
+    const int n0 = n * BN;
+    const int last = Lk - 1;
+#pragma unroll
+    for (int it = 0; it < K_LOADS; ++it) kphys[it] = table[min(n0 + (it * 256 + tid) / K_CH, last) / bs];
+#pragma unroll
+    for (int it = 0; it < V_LOADS; ++it) {
+      const int t0 = n0 + VPL * ((it * 256 + tid) % V_CH);
+      vphys[it] = table[min(t0, last & ~(VPL - 1)) / bs];
+    }
+  }
+  __device__ __forceinline__ void fetch(int n) {                // table entries of tile n are loaded
     const int tid = threadIdx.x;
     const int n0 = n * BN;
     tile0 = n0;
@@ -196,9 +221,8 @@ struct PagedLoader {
 #pragma unroll
     for (int it = 0; it < K_LOADS; ++it) {
       const int idx = it * 256 + tid;
-      const int key = n0 + idx / K_CH, ch = idx % K_CH;
-      const int kk = min(key, last);
-      const char* row = kc + (size_t)table[kk / bs] * block_stride + (size_t)(kk % bs) * D * ELT;
+      const int key = min(n0 + idx / K_CH, last), ch = idx % K_CH;
+      const char* row = kc + (size_t)kphys[it] * block_stride + (size_t)(key % bs) * D * ELT;
       kreg[it] = ld16(row + 16 * ch);                 // rows past the keys are zeroed in stage
     }
 #pragma unroll
@@ -206,10 +230,9 @@ struct PagedLoader {
       const int idx = it * 256 + tid;
       const int d = idx / V_CH, t0 = n0 + VPL * (idx % V_CH);
       const int tt = min(t0, last & ~(VPL - 1));          // a VPL-aligned run inside a valid page
-      const char* src = vc + (size_t)table[tt / bs] * block_stride + ((size_t)d * bs + tt % bs) * ELT;
-      u32x4 w = ld16(src);
-      vreg[it] = w;
+      vreg[it] = ld16(vc + (size_t)vphys[it] * block_stride + ((size_t)d * bs + tt % bs) * ELT);
     }
+    if ((n + 1) * BN < Lk) load_table(n + 1);
   }
   __device__ __forceinline__ void stage(bf16* Ks, bf16* Vt) {
     using S = PrefillShape<D, BN>;
