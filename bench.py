@@ -290,7 +290,7 @@ def main():
     if run("c4"):
         c4 = synth.config_case("c4", device=dev)
         best = None
-        for s in (0, 512):
+        for s in ((a.splits,) if a.splits else (0, 512)):
             r = decode_section(lib, c4, s, a.steps, a.warmup, f"decode c4 partitions={s or 'auto'}")
             if best is None or r["kernel_ms_mean"] < best["kernel_ms_mean"]:
                 best = r
@@ -299,7 +299,8 @@ def main():
             "workload": "split-KV decode, 2 x 131072 tokens, 32/2 heads, D 128, bf16 KV, 64-token blocks",
             "gbs": gbs, "partitions": best["splits"], "ms": best["kernel_ms_mean"],
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode_c4", ["common.h", "decode_core.h", "decode.hip"])}}
         if not a.quick:
             units = [(0, 0), (1, 17), (0, 31)]
             par = sampled_parity_paged(c4, best["out"], best["lse"], units)
@@ -321,7 +322,9 @@ def main():
             "decode_gbs": mx["decode_kv_bytes"] / mx["ms"] / 1e6,
             "algorithmic_flops": mx["flops"], "decode_kv_bytes": mx["decode_kv_bytes"],
             "prefill_kv_bytes": mx["prefill_kv_bytes"],
-            "roofline": {"bound": "mfma", "lower_bound_ms": mx["t_star_ms"], "frac": mx["t_star_ms"] / mx["ms"]}}
+            "roofline": {"bound": "mfma", "lower_bound_ms": mx["t_star_ms"], "frac": mx["t_star_ms"] / mx["ms"],
+                         "traffic": measured_traffic("mixed_c5", ["common.h", "decode_core.h", "decode.hip",
+                                                                  "prefill_core.h", "prefill.hip"])}}
         if not a.quick:
             n_pre = sum(1 for ql in c5.q_lens if ql > 1)
             units = [(0, 0), (n_pre - 1, 15), (n_pre, 3), (n_pre + 50, 9), (len(c5.q_lens) - 1, 12)]

@@ -1,0 +1,122 @@
+"""HBM traffic per call of the attention kernels, from hardware counters.
+
+Two sub-commands:
+
+  python bench_traffic.py copy
+      Launches a plain elementwise copy (fp32, 1 GiB read + 1 GiB written, 8 times) and nothing
+      else on the GPU. Profiled with `rocprofv3 --pmc FETCH_SIZE` and then `--pmc WRITE_SIZE`, it
+      gives what each counter reads for a known number of bytes.
+
+  python bench_traffic.py assemble --calib FETCH_CSV WRITE_CSV --case KEY FETCH_CSV WRITE_CSV [...]
+      Reads the rocprofv3 counter_collection.csv files of those runs and writes profiles/traffic.json:
+      for each case, the counters of every kernel of one library call (the partition kernel and the
+      merge kernel of a decode call, the prefill kernel, the mixed kernel and its merge), each
+      scaled by the copy's bytes-per-counter factor, summed per call. Each entry records a digest of
+      the kernel sources it was measured on; bench.py reports it only while the sources match.
+"""
+
+import argparse
+import csv
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+COPY_ELEMS = 1 << 28          # fp32 elements: 1 GiB each way
+COPY_REPS = 8
+
+# per case: the kernel-name fragments of one call, and the sources the kernels are built from
+CASES = {
+    "decode_paged_c2": (["decode_share_kernel", "decode_merge_kernel"], ["common.h", "decode_core.h", "decode.hip"]),
+    "decode_c4": (["decode_share_kernel", "decode_merge_kernel"], ["common.h", "decode_core.h", "decode.hip"]),
+    "prefill_c3": (["prefill_varlen_kernel"], ["common.h", "prefill_core.h", "prefill.hip"]),
+    "mixed_c5": (["varlen_mixed_kernel", "decode_merge_kernel"],
+                 ["common.h", "decode_core.h", "decode.hip", "prefill_core.h", "prefill.hip"]),
+}
+
+
+def run_copy():
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.empty(COPY_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(COPY_REPS):
+        torch.add(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel": "elementwise add (copy)", "bytes_read": 4 * COPY_ELEMS,
+                      "bytes_written": 4 * COPY_ELEMS, "dispatches": COPY_REPS}))
+
+
+def read_counter(path, counter):
+    """{kernel name: [value per dispatch]} for one counter of a counter_collection.csv."""
+    per = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return per
+
+
+def pick(per, fragment):
+    vals = [v for name, vs in per.items() if fragment in name for v in vs]
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel named like {fragment!r}")
+    return vals
+
+
+def assemble(a):
+    sys.path.insert(0, ROOT)
+    from bench import sources_digest
+    f_fetch = pick(read_counter(a.calib[0], "FETCH_SIZE"), "elementwise")
+    f_write = pick(read_counter(a.calib[1], "WRITE_SIZE"), "elementwise")
+    nbytes = 4 * COPY_ELEMS
+    # bytes per KiB that the counter reports (1024 if it counted every byte)
+    k_fetch = nbytes / statistics.median(f_fetch)
+    k_write = nbytes / statistics.median(f_write)
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table["_calibration"] = {
+        "copy": f"elementwise fp32 add, {nbytes} bytes read and {nbytes} written per dispatch",
+        "fetch_kib_per_dispatch": statistics.median(f_fetch), "write_kib_per_dispatch": statistics.median(f_write),
+        "bytes_per_fetch_kib": k_fetch, "bytes_per_write_kib": k_write}
+    for key, fcsv, wcsv in a.case:
+        kernels, sources = CASES[key]
+        fetch, write = read_counter(fcsv, "FETCH_SIZE"), read_counter(wcsv, "WRITE_SIZE")
+        per_kernel = {}
+        for frag in kernels:
+            fk, wk = pick(fetch, frag), pick(write, frag)
+            per_kernel[frag] = {"dispatches": len(fk), "fetch_kib_median": statistics.median(fk),
+                                "write_kib_median": statistics.median(wk),
+                                "read_bytes": statistics.median(fk) * k_fetch,
+                                "written_bytes": statistics.median(wk) * k_write}
+        table[key] = {"sources_sha256_16": sources_digest(sources), "kernels": per_kernel,
+                      "hbm_bytes_per_call": sum(v["read_bytes"] + v["written_bytes"] for v in per_kernel.values())}
+        print(f"{key}: {table[key]['hbm_bytes_per_call'] / 1e6:.1f} MB per call")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    sub.add_parser("copy")
+    asm = sub.add_parser("assemble")
+    asm.add_argument("--calib", nargs=2, required=True, metavar=("FETCH_CSV", "WRITE_CSV"))
+    asm.add_argument("--case", nargs=3, action="append", default=[], metavar=("KEY", "FETCH_CSV", "WRITE_CSV"))
+    a = ap.parse_args()
+    if a.cmd == "copy":
+        run_copy()
+    else:
+        assemble(a)
+
+
+if __name__ == "__main__":
+    main()
