@@ -82,6 +82,13 @@ __device__ __forceinline__ bf16x2 cvt_pk_bf16(float a, float b) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// max(x, x of lane l ^ 32) in every lane: one cross-half swap on the VALU (v_permlane32_swap
+// exchanges lanes 32-63 of its first operand with lanes 0-31 of its second), no LDS round trip.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ---- cross-lane reductions over lanes l, l^16, l^32, l^48 (the four k-slot groups of a
 // 16-wide MFMA column).
 __device__ __forceinline__ float max_over_quads(float x) {

@@ -392,7 +392,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) tmax = max3(tmax, st[kb][r], st[kb][r + 1]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      tmax = max_with_other_half(tmax);
       tmax = (tmax == kNegInf) ? kNegInf : tmax * c;
       // move the reference (and rescale what was accumulated) only where the tile maximum is
       // more than kLazyRescale above it; a row's first visible tile always moves it
@@ -410,17 +410,21 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
+          for (int t = 0; t < 2; ++t) {
+            {
+              float e[8];
 #pragma unroll
-            for (int s = 0; s < 8; s += 2) {
-              const float e0 = fast_exp2(__builtin_fmaf(st[kb][8 * t + s], c, nbase));
-              const float e1 = fast_exp2(__builtin_fmaf(st[kb][8 * t + s + 1], c, nbase));
-              l += e0;
-              l += e1;
-              const bf16x2 pe = cvt_pk_bf16(e0, e1);
-              pB[kb][t][s] = pe[0];
-              pB[kb][t][s + 1] = pe[1];
+              for (int s = 0; s < 8; ++s) e[s] = fast_exp2(__builtin_fmaf(st[kb][8 * t + s], c, nbase));
+#pragma unroll
+              for (int s = 0; s < 8; s += 2) {
+                const bf16x2 pe = cvt_pk_bf16(e[s], e[s + 1]);
+                pB[kb][t][s] = pe[0];
+                pB[kb][t][s + 1] = pe[1];
+              }
+              // pairwise sum: a short dependency chain instead of eight serial adds
+              l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
             }
+          }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const bf16* vrow = Vt + (32 * db + j) * S::VS + 8 * hh;
