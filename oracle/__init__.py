@@ -26,13 +26,16 @@ Modules:
   algorithms -- the pages' tiled algorithms written step by step (online
                 softmax over K blocks, split-KV + LSE merge), used only to pin
                 the pages' claim that they reach the plain definition exactly.
+  cache      -- appending new tokens to a paged cache: a token-by-token scatter, with the
+                e4m3fn quantiser for fp8 caches.
   parallel   -- a process pool over (request, head) units, for timing only.
 
 Pins: every public function is checked in ``tests/test_oracle_*.py`` against
 closed forms, brute force, a library routine or the pages' worked example.
 """
 
-from .formats import decode_bf16_bits, decode_e4m3fn, E4M3FN_MAX
+from .formats import decode_bf16_bits, decode_e4m3fn, encode_e4m3fn, E4M3FN_MAX
+from .cache import kv_append_paged, quantize_e4m3fn
 from .attention import (
     attend,
     prefill_varlen,
@@ -45,6 +48,9 @@ from .algorithms import online_softmax_attend, split_kv_attend, merge_partials
 __all__ = [
     "decode_bf16_bits",
     "decode_e4m3fn",
+    "encode_e4m3fn",
+    "quantize_e4m3fn",
+    "kv_append_paged",
     "E4M3FN_MAX",
     "attend",
     "prefill_varlen",

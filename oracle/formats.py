@@ -40,3 +40,30 @@ def decode_e4m3fn(codes) -> np.ndarray:
     value = np.where(exp_field == 0, subnormal, normal)
     is_nan = (exp_field == 0xF) & ((c & 0x7) == 0x7)
     return np.where(is_nan, np.nan, value)
+
+
+def encode_e4m3fn(x) -> np.ndarray:
+    """Finite floats (any shape) -> uint8 OCP e4m3fn codes: the nearest representable value,
+    ties to the code with an even mantissa, magnitudes beyond 448 saturated to 448.
+
+    Written from the definition: the 127 non-negative finite codes are decoded (they increase
+    with the code), the magnitude is placed between its two neighbours, and the nearer one is
+    taken (on a tie, the one whose last mantissa bit is 0). The sign bit is copied (so -0.0
+    gives 0x80). The caller computes x in the precision its quantiser uses.
+    """
+    a = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(a)):
+        raise ValueError("encode_e4m3fn takes finite values only")
+    codes = np.arange(0x7F, dtype=np.uint8)                  # 0x00 .. 0x7E: +0 .. 448
+    values = decode_e4m3fn(codes)
+    mag = np.minimum(np.abs(a), E4M3FN_MAX)
+    hi = np.searchsorted(values, mag, side="left")          # first value >= mag
+    hi = np.minimum(hi, len(values) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = mag - values[lo]
+    d_hi = values[hi] - mag
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((codes[hi] & 1) == 0))
+    code = np.where(take_hi, codes[hi], codes[lo]).astype(np.uint8)
+    code = np.where(mag == values[hi], codes[hi], code).astype(np.uint8)   # exact hits
+    sign = np.signbit(a)
+    return np.where(sign, code | np.uint8(0x80), code).astype(np.uint8)
