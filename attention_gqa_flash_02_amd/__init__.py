@@ -25,6 +25,7 @@ __all__ = [
     "attn_decode_paged",
     "attn_varlen_workspace_bytes",
     "attn_varlen_paged",
+    "attn_kv_append_paged",
     "library_path",
 ]
 
@@ -195,3 +196,38 @@ def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k
     if st != 0:
         raise AttnError(st, "attn_varlen_paged")
     return out, lse
+
+
+def attn_kv_append_paged(k_new, v_new, k_cache, v_cache, block_table, cu_seqlens_new, seq_lens_k,
+                         k_scale=None, v_scale=None, stream=None):
+    """Write new tokens' K/V (k_new, v_new [T_new, Hkv, D] bf16) into a paged cache in place:
+    request b's rows cu_seqlens_new[b] .. cu_seqlens_new[b+1]-1 become its last cached tokens
+    (seq_lens_k counts them). k_cache [N, Hkv, bs, D] / v_cache [N, Hkv, D, bs] are bf16, or uint8 /
+    float8_e4m3fn codes quantised with k_scale / v_scale [Hkv] fp32."""
+    dev = k_new.device
+    _check(k_new, "k_new", torch.bfloat16, dev)
+    _check(v_new, "v_new", torch.bfloat16, dev)
+    kvt = _kv_dtype(k_cache)
+    if _kv_dtype(v_cache) != kvt:
+        raise TypeError("k_cache and v_cache must have the same dtype")
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    _check(block_table, "block_table", torch.int32, dev)
+    _check(cu_seqlens_new, "cu_seqlens_new", torch.int32, dev)
+    _check(seq_lens_k, "seq_lens_k", torch.int32, dev)
+    if kvt == ATTN_KV_FP8_E4M3FN:
+        _check(k_scale, "k_scale", torch.float32, dev)
+        _check(v_scale, "v_scale", torch.float32, dev)
+    t_new, hkv, d = k_new.shape
+    if tuple(v_new.shape) != (t_new, hkv, d):
+        raise ValueError("k_new and v_new must have the same shape")
+    nblk, hkv_c, bs, d_c = k_cache.shape
+    if (hkv_c, d_c) != (hkv, d) or tuple(v_cache.shape) != (nblk, hkv, d, bs):
+        raise ValueError("cache shapes do not match k_new")
+    st = _lib.load().attn_kv_append_paged(
+        _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), kvt, _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), _ptr(cu_seqlens_new), _ptr(seq_lens_k), seq_lens_k.numel(), t_new, hkv, d, bs,
+        nblk, block_table.shape[1], _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_kv_append_paged")

@@ -27,6 +27,9 @@ SIGNATURES = {
     "attn_varlen_paged": (c_i32, [c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_i32, c_f32, c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                   c_i32, c_i32, c_i32, c_i32, c_i32, c_void_p, c_size, c_void_p]),
+    "attn_kv_append_paged": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                     c_void_p]),
 }
 
 _lib = None

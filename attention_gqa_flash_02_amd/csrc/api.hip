@@ -262,4 +262,43 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+
+attn_status attn_kv_append_paged(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 int32_t kv_dtype, const float* k_scale, const float* v_scale,
+                                 const int32_t* block_table, const int32_t* cu_seqlens_new,
+                                 const int32_t* seq_lens_k, int32_t num_seqs, int32_t total_new,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, int32_t max_blocks_per_seq, void* stream) {
+  if (!k_cache || !v_cache || !block_table || !cu_seqlens_new || !seq_lens_k) return ATTN_ERR_NULL;
+  if (kv_dtype != ATTN_KV_BF16 && kv_dtype != ATTN_KV_FP8_E4M3FN) return ATTN_ERR_UNSUPPORTED;
+  if (kv_dtype == ATTN_KV_FP8_E4M3FN && (!k_scale || !v_scale)) return ATTN_ERR_NULL;
+  if (num_seqs <= 0 || total_new < 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return ATTN_ERR_SHAPE;
+  if (head_dim != 128 && head_dim != 256) return ATTN_ERR_UNSUPPORTED;
+  if (!supported_block_size(block_size)) return ATTN_ERR_UNSUPPORTED;
+  if (num_seqs > kMaxPagedSeqs) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size > INT_MAX / 2) return ATTN_ERR_SHAPE;
+  if (total_new == 0) return ATTN_OK;                // the new rows may then be NULL
+  if (!k_new || !v_new) return ATTN_ERR_NULL;
+  AppendParams p{};
+  p.k_new = static_cast<const bf16*>(k_new);
+  p.v_new = static_cast<const bf16*>(v_new);
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_table = block_table;
+  p.cu_seqlens_new = cu_seqlens_new;
+  p.seq_lens_k = seq_lens_k;
+  p.num_seqs = num_seqs;
+  p.total_new = total_new;
+  p.Hkv = num_kv_heads;
+  p.bs = block_size;
+  p.max_blocks = max_blocks_per_seq;
+  (void)num_blocks;
+  hipError_t e = launch_append(p, head_dim, kv_dtype == ATTN_KV_BF16 ? KV_BF16 : KV_FP8,
+                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -29,6 +29,22 @@ hipError_t launch_decode_merge(const PagedParams& p, int head_dim, int nu, int r
 hipError_t launch_mixed(const PrefillParams& pp, const PagedParams& dp, int head_dim, int kv_type, int total_q,
                         hipStream_t stream);
 
+// Paged KV-cache append: new tokens' K rows / V columns into their cache slots (fp8 caches get
+// the values quantised with the per-head scales).
+struct AppendParams {
+  const bf16* k_new;           // [total_new, Hkv, D]
+  const bf16* v_new;           // [total_new, Hkv, D]
+  void* k_cache;               // [num_blocks, Hkv, bs, D] bf16 or e4m3fn codes
+  void* v_cache;               // [num_blocks, Hkv, D, bs]
+  const float* k_scale;        // [Hkv] (fp8) or nullptr
+  const float* v_scale;        // [Hkv] (fp8) or nullptr
+  const int32_t* block_table;  // [B, max_blocks]
+  const int32_t* cu_seqlens_new;  // [B + 1]
+  const int32_t* seq_lens_k;   // [B] cached tokens after the append
+  int num_seqs, total_new, Hkv, bs, max_blocks;
+};
+hipError_t launch_append(const AppendParams& p, int head_dim, int kv_type, hipStream_t stream);
+
 // Keys per chunk of the decode variant, and its resident workgroups per compute unit.
 int decode_chunk_tokens(int head_dim, int kv_type);
 int decode_wgs_per_cu(int head_dim, int kv_type);

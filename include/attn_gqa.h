@@ -174,6 +174,41 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
                               int32_t num_splits, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Append new tokens' K and V to a paged cache, the step before attention in
+ * every engine step ("Optimization 1: batching and attention", section 3.4:
+ * the cache is a pool of fixed-size blocks reached through a block table;
+ * "Attention kernels", section "Paged KV and kernels": an FP8 cache is read
+ * directly by the attention kernels).
+ * Request b's new tokens are rows cu_seqlens_new[b] .. cu_seqlens_new[b+1]-1
+ * of k_new / v_new (n_b of them); they become its cached tokens
+ * seq_lens_k[b] - n_b .. seq_lens_k[b] - 1 (seq_lens_k counts them, as the
+ * attention calls do). Token t goes to slot t % block_size of physical block
+ * block_table[b][t / block_size]: the K row [block][h][slot][:] and the V
+ * column [block][h][:][slot] (layouts as above). No other byte of the caches
+ * changes.
+ *   k_new, v_new [total_new, num_kv_heads, head_dim] bf16 (device, read only)
+ *   k_cache, v_cache: bf16 (ATTN_KV_BF16: the values are stored unchanged) or
+ *     e4m3fn codes (ATTN_KV_FP8_E4M3FN: code = e4m3fn(x / scale[h]), the
+ *     quotient in correctly rounded fp32, rounded to the nearest code with ties
+ *     to even, magnitudes beyond 448 saturated); k_scale, v_scale [num_kv_heads]
+ *     fp32 (device), required for fp8, ignored for bf16.
+ *   cu_seqlens_new [num_seqs + 1], seq_lens_k [num_seqs] int32 (device).
+ * Device-resident values are the caller's contract as for the attention calls;
+ * in addition n_b <= seq_lens_k[b], distinct new tokens must map to distinct
+ * slots, and the new rows must not alias the caches. total_new = 0 is a no-op
+ * (k_new and v_new may then be NULL).
+ * Errors: ATTN_ERR_NULL (a required pointer is NULL), ATTN_ERR_SHAPE (counts
+ * out of range), ATTN_ERR_UNSUPPORTED (head_dim, block_size, kv dtype or more
+ * than 16384 requests).
+ */
+attn_status attn_kv_append_paged(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 int32_t kv_dtype, const float* k_scale, const float* v_scale,
+                                 const int32_t* block_table, const int32_t* cu_seqlens_new,
+                                 const int32_t* seq_lens_k, int32_t num_seqs, int32_t total_new,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, int32_t max_blocks_per_seq, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

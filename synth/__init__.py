@@ -31,6 +31,8 @@ from .cases import (
     PagedCase,
     make_prefill,
     make_paged,
+    AppendCase,
+    make_append,
     CONFIGS,
     config_case,
 )
@@ -38,6 +40,8 @@ from .cases import (
 __all__ = [
     "PrefillCase",
     "PagedCase",
+    "AppendCase",
+    "make_append",
     "make_prefill",
     "make_paged",
     "CONFIGS",

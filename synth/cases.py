@@ -246,3 +246,64 @@ def config_case(name, shrink=1, device="cpu", poison=POISON_FINITE):
         return make_paged(5, kv_lens, q_lens, 16, 4, 256, 16, kv_format="e4m3fn", device=device,
                           poison=poison, lengths_drawn=gen)
     raise KeyError(name)
+
+
+@dataclass
+class AppendCase:
+    """New tokens to write into a paged cache that already holds each request's prior tokens."""
+    k_new: torch.Tensor            # [T_new, Hkv, D] bf16
+    v_new: torch.Tensor            # [T_new, Hkv, D] bf16
+    k_cache: torch.Tensor          # [N, Hkv, bs, D] bf16 or uint8 codes (random prior content)
+    v_cache: torch.Tensor          # [N, Hkv, D, bs]
+    k_scale: torch.Tensor          # [Hkv] fp32 or None
+    v_scale: torch.Tensor
+    block_table: torch.Tensor      # [B, max_blocks] int32
+    cu_seqlens_new: torch.Tensor   # [B + 1] int32
+    seq_lens_k: torch.Tensor       # [B] int32, prior + new
+    prior_lens: list
+    new_lens: list
+    block_size: int
+    kv_format: str
+
+
+def make_append(seed, prior_lens, new_lens, num_kv_heads, head_dim, block_size, kv_format="bf16",
+                value_std=1.0, scales=None):
+    """Seeded append case. Draw order: page permutation -> prior cache content -> K_new -> V_new.
+
+    The cache pool holds every request's blocks (prior + new tokens) plus spare blocks, in
+    randperm order; its prior content is random bf16 bits / fp8 codes (any byte the append must
+    not touch). New values are N(0, value_std) rounded to bf16. fp8 scales default to per-head
+    values spread over [0.002, 0.05] (so that some quotients saturate and some are subnormal).
+    """
+    g = torch.Generator().manual_seed(seed)
+    lens = [p + n for p, n in zip(prior_lens, new_lens)]
+    nblocks = [max(1, -(-L // block_size)) for L in lens]
+    spare = max(2, sum(nblocks) // 20)
+    pool = sum(nblocks) + spare
+    perm = torch.randperm(pool, generator=g)
+    max_blocks = max(nblocks)
+    table = torch.zeros((len(lens), max_blocks), dtype=torch.int32)
+    used = 0
+    for b, nb in enumerate(nblocks):
+        table[b, :nb] = perm[used:used + nb].to(torch.int32)
+        used += nb
+    fp8 = kv_format != "bf16"
+    if fp8:
+        k_cache = torch.randint(0, 0x7F, (pool, num_kv_heads, block_size, head_dim), generator=g, dtype=torch.uint8)
+        v_cache = torch.randint(0, 0x7F, (pool, num_kv_heads, head_dim, block_size), generator=g, dtype=torch.uint8)
+    else:
+        k_cache = (torch.randn((pool, num_kv_heads, block_size, head_dim), generator=g)).to(torch.bfloat16)
+        v_cache = (torch.randn((pool, num_kv_heads, head_dim, block_size), generator=g)).to(torch.bfloat16)
+    t_new = sum(new_lens)
+    k_new = (torch.randn((t_new, num_kv_heads, head_dim), generator=g) * value_std).to(torch.bfloat16)
+    v_new = (torch.randn((t_new, num_kv_heads, head_dim), generator=g) * value_std).to(torch.bfloat16)
+    k_scale = v_scale = None
+    if fp8:
+        if scales is None:
+            scales = torch.linspace(0.002, 0.05, 2 * num_kv_heads, dtype=torch.float32)
+        scales = torch.as_tensor(scales, dtype=torch.float32)
+        k_scale, v_scale = scales[:num_kv_heads].clone(), scales[num_kv_heads:2 * num_kv_heads].clone()
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    cu[1:] = torch.tensor(new_lens, dtype=torch.int32).cumsum(0)
+    return AppendCase(k_new, v_new, k_cache, v_cache, k_scale, v_scale, table, cu,
+                      torch.tensor(lens, dtype=torch.int32), list(prior_lens), list(new_lens), block_size, kv_format)

@@ -102,3 +102,27 @@ def test_varlen_validation():
     st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None,
                                2, 10, 11, 8, 2, 128, 16, 10, 4, 1, None, 0, None)
     assert st == 2                                   # max_q_len > total_q
+
+
+def _append(**kw):
+    a = dict(kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, kvt=0, ks=None, vs=None, table=FAKE, cu=FAKE, lens=FAKE,
+             nseq=2, total=5, hkv=2, d=128, bs=16, nblk=10, maxblk=4)
+    a.update(kw)
+    return _lib.load().attn_kv_append_paged(a["kn"], a["vn"], a["kc"], a["vc"], a["kvt"], a["ks"], a["vs"],
+                                            a["table"], a["cu"], a["lens"], a["nseq"], a["total"], a["hkv"],
+                                            a["d"], a["bs"], a["nblk"], a["maxblk"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), 1), (dict(vc=None), 1), (dict(cu=None), 1), (dict(lens=None), 1), (dict(table=None), 1),
+    (dict(kvt=1), 1),                               # fp8 without scales
+    (dict(kvt=3), 3), (dict(d=64), 3), (dict(bs=8), 3), (dict(nseq=16385), 3),
+    (dict(nseq=0), 2), (dict(total=-1), 2), (dict(hkv=0), 2), (dict(nblk=0), 2), (dict(maxblk=0), 2),
+])
+def test_append_validation(kw, code):
+    assert _append(**kw) == code
+
+
+def test_append_nothing_is_a_noop():
+    assert _append(total=0) == 0
+    assert _append(total=0, kn=None, vn=None) == 0

@@ -1,0 +1,71 @@
+"""Paged KV-cache append on the GPU against the oracle's token-by-token scatter: every byte of
+both caches must match (the appended slots bit-exactly, including the e4m3fn codes, and every
+other byte unchanged)."""
+
+import numpy as np
+import pytest
+import torch
+
+import attention_gqa_flash_02_amd as lib
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _np_bits(t):
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.view(torch.uint8).numpy()
+
+
+def _check(case, gpu):
+    dev = {k: (v.to(gpu) if isinstance(v, torch.Tensor) else v) for k, v in vars(case).items()}
+    kc, vc = dev["k_cache"].clone(), dev["v_cache"].clone()
+    lib.attn_kv_append_paged(dev["k_new"], dev["v_new"], kc, vc, dev["block_table"], dev["cu_seqlens_new"],
+                             dev["seq_lens_k"], k_scale=dev["k_scale"], v_scale=dev["v_scale"])
+    torch.cuda.synchronize()
+    fmt = "bf16" if case.kv_format == "bf16" else "e4m3fn"
+    ks = None if case.k_scale is None else case.k_scale.numpy()
+    vs = None if case.v_scale is None else case.v_scale.numpy()
+    ref_k, ref_v = oracle.kv_append_paged(_np_bits(case.k_cache), _np_bits(case.v_cache), _np_bits(case.k_new),
+                                          _np_bits(case.v_new), case.block_table.numpy(),
+                                          case.cu_seqlens_new.numpy(), case.seq_lens_k.numpy(), kv_format=fmt,
+                                          k_scale=ks, v_scale=vs)
+    got_k, got_v = _np_bits(kc), _np_bits(vc)
+    bad_k = np.argwhere(got_k != ref_k)
+    bad_v = np.argwhere(got_v != ref_v)
+    assert bad_k.size == 0, f"K differs at {bad_k[:5].tolist()} ({len(bad_k)} elements)"
+    assert bad_v.size == 0, f"V differs at {bad_v[:5].tolist()} ({len(bad_v)} elements)"
+
+
+@pytest.mark.parametrize("kv_format", ["bf16", "e4m3fn"])
+@pytest.mark.parametrize("d,bs,hkv", [(128, 16, 2), (256, 16, 4), (128, 64, 1), (256, 32, 2)])
+def test_append_mixed_batch(gpu, kv_format, d, bs, hkv):
+    # decode tokens, chunks crossing page boundaries, an empty request, a first fill
+    prior = [0, 5, 16, 100, 7, 0, 31, 250]
+    new = [1, 3, 17, 64, 0, 130, 1, 45]
+    case = synth.make_append(200 + d + bs, prior, new, hkv, d, bs, kv_format, value_std=2.0)
+    _check(case, gpu)
+
+
+def test_append_many_requests_and_rounding_ties(gpu):
+    # 700 requests (the row -> request search crosses its LDS window), mostly single tokens with
+    # runs of empty requests; one head's scale is 1 so that quotients hit e4m3 midpoints exactly
+    g = np.random.default_rng(5)
+    new = [int(x) for x in g.choice([0, 0, 0, 1, 1, 2, 40], size=700)]
+    prior = [int(x) for x in g.integers(0, 300, size=700)]
+    case = synth.make_append(77, prior, new, 2, 128, 16, "e4m3fn", value_std=40.0, scales=[1.0, 0.01, 1.0, 0.3])
+    # overwrite some new values with exact e4m3 midpoints (representable in bf16) and saturating values
+    vals = oracle.decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    flat = case.k_new.view(-1, case.k_new.shape[-1])
+    take = torch.from_numpy(np.concatenate([mids, -mids, [500.0, -1e4, 0.0]]).astype(np.float32)).to(torch.bfloat16)
+    flat[: (take.numel() + 127) // 128].view(-1)[: take.numel()] = take
+    _check(case, gpu)
+
+
+def test_append_empty_is_a_noop(gpu):
+    case = synth.make_append(3, [4, 9], [0, 0], 2, 128, 16, "bf16")
+    _check(case, gpu)
