@@ -9,11 +9,12 @@ that no step finds it in the 256 MB last-level cache). The same run also times
 the causal varlen prefill (4 x 8192 tokens, 32/8 heads, D 128), the
 long-context split-KV decode (2 x 131072 tokens, 32/2 heads, 64-token blocks)
 and the mixed fp8 batch (8 prefill chunks of 2048 over cached prefixes + 120
-decodes, 16/4 heads, D 256), reports each against its roofline, checks sampled
+decodes, 16/4 heads, D 256) and the KV-cache append of that step, reports each against its
+roofline, checks sampled
 outputs against the fp64 oracle, and times the oracle itself on the host cores
 (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c2|c3|c4|c5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c2|c3|c4|c5|append]
                        [--no-cpu-baseline] [--quick]
 Prints one JSON line.
 """
@@ -46,7 +47,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--splits", type=int, default=0, help="decode partitions (0 = library choice)")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "append"], default=None,
                     help="time one workload only (for profiling); the JSON line still names c2's metric")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the parity samples")
@@ -183,6 +184,71 @@ def mixed_section(lib, case, steps, warmup):
             "wall_ms": wall, "t_star_ms": t_star, "out": out, "lse": lse}
 
 
+def multi_token_section(lib, case, steps, warmup, q_len=4):
+    """Speculative-verification decode on the batch-32 cache: each request's last q_len cached
+    tokens are new query rows (g * q_len = 16 rows per KV head, one decode-path partition set),
+    through the mixed varlen call. Algorithmic bytes: the K/V bytes, as for the decode."""
+    import torch
+    from attention_gqa_flash_02_amd import workmodel
+    dev = case.q.device
+    b, hq, d = case.q.shape
+    g = torch.Generator().manual_seed(21)
+    q = torch.randn((b * q_len, hq, d), generator=g).to(torch.bfloat16).to(dev)
+    cu = torch.arange(0, b * q_len + 1, q_len, dtype=torch.int32, device=dev)
+    kv_bytes = workmodel.kv_bytes(case.kv_lens, case.num_kv_heads, d, 2)
+    s = lib.attn_decode_num_splits(b, case.num_kv_heads, d, 0, case.block_size, case.block_table.shape[1], 0)
+    ws = torch.empty(lib.attn_varlen_workspace_bytes(b, case.num_kv_heads, d, s), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+
+    def call():
+        lib.attn_varlen_paged(q, case.k_cache, case.v_cache, case.block_table, cu, case.seq_lens_k, True, case.scale,
+                              out=out, max_q_len=q_len, num_splits=s, workspace=ws)
+    wall, durs = time_steps([call], steps, warmup)
+    kern = statistics.mean(durs)
+    gbs = kv_bytes / kern / 1e6
+    log(f"[bench] multi-token decode q_len={q_len}: call mean={kern * 1e3:.1f} us -> {gbs:.0f} GB/s")
+    return {"workload": f"batch-32 paged decode cache (32/8 heads, D 128, bf16, 16-token pages), {q_len} new "
+                        f"query rows per request (g * q_len = 16 rows per KV head)",
+            "q_len": q_len, "kv_bytes": kv_bytes, "ms": kern, "wall_ms": wall, "gbs": gbs,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+
+
+def append_section(lib, steps, warmup):
+    """The KV-cache append of one mixed step at the c5 geometry: 8 prefill chunks of 2048 new
+    tokens over prefixes U[0, 32768] and 120 decode tokens over contexts U[512, 32768]; 4 KV heads,
+    head_dim 256, bs 16, written as fp8 e4m3fn with per-head scales. Algorithmic bytes: the new
+    bf16 K and V read once, their fp8 codes written once."""
+    import torch
+    import synth
+    g = torch.Generator().manual_seed(5)
+    prior = [int(x) for x in torch.randint(0, 32769, (8,), generator=g)] + \
+            [int(x) - 1 for x in torch.randint(512, 32769, (120,), generator=g)]
+    new = [2048] * 8 + [1] * 120
+    case = synth.make_append(5, prior, new, 4, 256, 16, "e4m3fn", cache_content=False)
+    dev = torch.device("cuda:0")
+    pool = int(case.block_table.max()) + 1
+    kc = torch.empty((pool, 4, 16, 256), dtype=torch.uint8, device=dev)
+    vc = torch.empty((pool, 4, 256, 16), dtype=torch.uint8, device=dev)
+    t = {k: v.to(dev) for k, v in vars(case).items() if isinstance(v, torch.Tensor)}
+
+    def call():
+        lib.attn_kv_append_paged(t["k_new"], t["v_new"], kc, vc, t["block_table"], t["cu_seqlens_new"],
+                                 t["seq_lens_k"], k_scale=t["k_scale"], v_scale=t["v_scale"])
+    wall, durs = time_steps([call], steps, warmup)
+    kern = statistics.mean(durs)
+    tn = sum(new)
+    nbytes = tn * 4 * 256 * 2 * 2 + tn * 4 * 256 * 1 * 2
+    gbs = nbytes / kern / 1e6
+    log(f"[bench] append c5 geometry: {tn} tokens, call mean={kern * 1e3:.1f} us -> {gbs:.0f} GB/s")
+    return {"workload": "KV-cache append of a mixed step: 8 x 2048 + 120 x 1 new tokens, 4 KV heads, D 256, "
+                        "bf16 in, fp8 e4m3fn out (per-head scales), 16-token pages",
+            "tokens": tn, "bytes": nbytes, "ms": kern, "wall_ms": wall, "gbs": gbs,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("append_c5", ["append.hip"])}}
+
+
 def parity_stats(out, lse, ref_o, ref_l):
     import numpy as np
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -265,6 +331,7 @@ def main():
             par = sampled_parity_paged(c2_host, dec["out"], dec["lse"], units)
             log(f"[bench] decode c2 parity on {par['units']} sampled (request, head) units: {par}")
             extra["decode_parity_sample"] = par
+        extra["multi_token_decode"] = multi_token_section(lib, c2, a.steps, a.warmup)
         del c2
         torch.cuda.empty_cache()
 
@@ -333,6 +400,9 @@ def main():
             extra["mixed_c5"]["parity_sample"] = par
         del c5, mx
         torch.cuda.empty_cache()
+
+    if run("append"):
+        extra["append_c5"] = append_section(lib, a.steps, a.warmup)
 
     cpu = None
     if not a.no_cpu_baseline and run("c2"):

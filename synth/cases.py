@@ -267,13 +267,15 @@ class AppendCase:
 
 
 def make_append(seed, prior_lens, new_lens, num_kv_heads, head_dim, block_size, kv_format="bf16",
-                value_std=1.0, scales=None):
+                value_std=1.0, scales=None, cache_content=True):
     """Seeded append case. Draw order: page permutation -> prior cache content -> K_new -> V_new.
 
     The cache pool holds every request's blocks (prior + new tokens) plus spare blocks, in
     randperm order; its prior content is random bf16 bits / fp8 codes (any byte the append must
     not touch). New values are N(0, value_std) rounded to bf16. fp8 scales default to per-head
     values spread over [0.002, 0.05] (so that some quotients saturate and some are subnormal).
+    With cache_content=False the caches are left as None (the pool size is
+    block_table.max() + 1 or more) and no prior content is drawn.
     """
     g = torch.Generator().manual_seed(seed)
     lens = [p + n for p, n in zip(prior_lens, new_lens)]
@@ -288,7 +290,10 @@ def make_append(seed, prior_lens, new_lens, num_kv_heads, head_dim, block_size, 
         table[b, :nb] = perm[used:used + nb].to(torch.int32)
         used += nb
     fp8 = kv_format != "bf16"
-    if fp8:
+    if not cache_content:                    # timing only: the caller allocates the pool
+        k_cache = v_cache = None
+        kshape = (pool, num_kv_heads, block_size, head_dim)
+    elif fp8:
         k_cache = torch.randint(0, 0x7F, (pool, num_kv_heads, block_size, head_dim), generator=g, dtype=torch.uint8)
         v_cache = torch.randint(0, 0x7F, (pool, num_kv_heads, head_dim, block_size), generator=g, dtype=torch.uint8)
     else:

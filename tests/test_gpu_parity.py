@@ -157,3 +157,17 @@ def test_varlen_group_sizes(gpu, hq, hkv):
     out, lse = _run_varlen(case)
     ref_o, ref_l = oracle_paged(case)
     compare(out, lse, ref_o, ref_l, label=f"varlen hq={hq} hkv={hkv}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (16, 4), (16, 2)])
+def test_varlen_multi_token_decode(gpu, hq, hkv):
+    """Speculative verification: 2-8 new query rows per request over a long cache; rows that fit
+    16 per KV head go through the split-KV decode path, the others through the prefill path."""
+    q_lens = [2, 3, 4, 5, 6, 7, 8, 1]
+    kv_lens = [900, 2000, 64, 17, 3000, 33, 1500, 700]
+    gen = torch.Generator().manual_seed(300 + hq + hkv)
+    case = _to(synth.make_paged(300 + hq + hkv, kv_lens, q_lens, hq, hkv, 128, 16, lengths_drawn=gen), gpu)
+    for splits in (0, 5):
+        out, lse = _run_varlen(case, splits)
+        ref_o, ref_l = oracle_paged(case)
+        compare(out, lse, ref_o, ref_l, label=f"multi-token hq={hq} hkv={hkv} splits={splits}")
