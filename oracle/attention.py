@@ -23,7 +23,10 @@ Readings where the pages say nothing (each is listed in the design doc):
     sits in physical block block_table[b, t // block_size], slot
     t % block_size ("Optimization 1", section 3.4; "Attention kernels",
     section "Paged KV and kernels");
-  * decode seq_lens count every cached token including the current one.
+  * decode seq_lens count every cached token including the current one;
+  * sliding window W > 0 (a lower bound on the visible keys, "Optimization 1", section 2 on
+    shrinking the effective KV; the NVIDIA guideline summary, principle 3): row i drops the keys
+    j < (Lk - Lq) + i - W + 1, the same bottom-right alignment as the causal bound.
 """
 
 import numpy as np
@@ -31,10 +34,12 @@ import numpy as np
 from .formats import decode_bf16_bits, decode_e4m3fn
 
 
-def attend(q, k, v, scale, causal):
+def attend(q, k, v, scale, causal, window=0):
     """One (request, query head): q [Lq, D], k [Lk, D], v [Lk, D] float64.
 
     Returns (o [Lq, D], lse [Lq]). Bottom-right causal alignment when ``causal``.
+    window > 0 (sliding window): row i also drops the keys j < (Lk - Lq) + i - window + 1,
+    i.e. with ``causal`` it sees its own position and the window - 1 keys before it.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -44,10 +49,12 @@ def attend(q, k, v, scale, causal):
     if lk == 0:
         return np.zeros((lq, dv)), np.full(lq, -np.inf)
     s = scale * (q @ k.T)                                   # S = scale * Q K^T, [Lq, Lk]
+    i = np.arange(lq)[:, None]
+    j = np.arange(lk)[None, :]
     if causal:
-        i = np.arange(lq)[:, None]
-        j = np.arange(lk)[None, :]
         s = np.where(j <= (lk - lq) + i, s, -np.inf)
+    if window > 0:
+        s = np.where(j >= (lk - lq) + i - window + 1, s, -np.inf)
     m = s.max(axis=1)                                       # row maximum
     empty = ~np.isfinite(m)                                 # rows with no visible key
     m_safe = np.where(empty, 0.0, m)
@@ -68,7 +75,7 @@ def _units(num_requests, num_q_heads, units):
     return [(int(b), int(h)) for b, h in units]
 
 
-def prefill_varlen(q, k, v, cu_seqlens, causal, scale, units=None):
+def prefill_varlen(q, k, v, cu_seqlens, causal, scale, units=None, window=0):
     """Varlen self-attention over contiguous K/V.
 
     q [T, Hq, D], k/v [T, Hkv, D] float64; cu_seqlens [B+1] (request b owns
@@ -90,7 +97,7 @@ def prefill_varlen(q, k, v, cu_seqlens, causal, scale, units=None):
     for b, h in _units(len(cu) - 1, hq, units):
         lo, hi = cu[b], cu[b + 1]
         kvh = h // g
-        o_bh, lse_bh = attend(q[lo:hi, h], k[lo:hi, kvh], v[lo:hi, kvh], scale, causal)
+        o_bh, lse_bh = attend(q[lo:hi, h], k[lo:hi, kvh], v[lo:hi, kvh], scale, causal, window)
         out[lo:hi, h] = o_bh
         lse[lo:hi, h] = lse_bh
     return out, lse
@@ -129,7 +136,7 @@ def _decode_rows(raw, kv_format, head_scale):
 
 
 def varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k, causal, scale,
-                 kv_format="bf16", k_scale=None, v_scale=None, units=None):
+                 kv_format="bf16", k_scale=None, v_scale=None, units=None, window=0):
     """Mixed varlen batch over a paged KV cache (prefill chunks and decode rows alike).
 
     q [Tq, Hq, D] float64; request b owns query rows cu_seqlens_q[b]:cu_seqlens_q[b+1]
@@ -160,14 +167,14 @@ def varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k, cau
                               _decode_rows(v_raw, kv_format, vs[kvh]))}
         k_rows, v_rows = gathered[key]
         lo, hi = cuq[b], cuq[b + 1]
-        o_bh, lse_bh = attend(q[lo:hi, h], k_rows, v_rows, scale, causal)
+        o_bh, lse_bh = attend(q[lo:hi, h], k_rows, v_rows, scale, causal, window)
         out[lo:hi, h] = o_bh
         lse[lo:hi, h] = lse_bh
     return out, lse
 
 
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale,
-                 kv_format="bf16", k_scale=None, v_scale=None, units=None):
+                 kv_format="bf16", k_scale=None, v_scale=None, units=None, window=0):
     """One query token per request over its paged cache: q [B, Hq, D] -> out [B, Hq, D], lse [B, Hq].
 
     The query is the newest cached token, so it sees all seq_lens[b] keys
@@ -177,4 +184,4 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale,
     nb = q.shape[0]
     cu = np.arange(nb + 1)
     return varlen_paged(q, k_cache, v_cache, block_table, cu, seq_lens, True, scale,
-                        kv_format, k_scale, v_scale, units)
+                        kv_format, k_scale, v_scale, units, window)

@@ -386,3 +386,60 @@ def test_pin14_fp8_cache_decoding_with_scales():
     o2, lse2 = oa.decode_paged(q, kf, vf, table, [6], 1.0, kv_format="f64")
     np.testing.assert_array_equal(o, o2)
     np.testing.assert_array_equal(lse, lse2)
+
+
+# ---- sliding window (a lower bound on the visible keys, bottom-right aligned)
+
+def test_window_covering_all_keys_equals_no_window():
+    g = np.random.default_rng(41)
+    q, k, v = g.normal(size=(7, 8)), g.normal(size=(19, 8)), g.normal(size=(19, 8))
+    for causal in (True, False):
+        o0, l0 = oa.attend(q, k, v, 0.3, causal)
+        o1, l1 = oa.attend(q, k, v, 0.3, causal, window=19 + 7)
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_window_one_sees_only_its_own_key():
+    g = np.random.default_rng(42)
+    q, k, v = g.normal(size=(6, 4)), g.normal(size=(10, 4)), g.normal(size=(10, 4))
+    o, l = oa.attend(q, k, v, 0.5, True, window=1)
+    own = np.arange(6) + 4                                   # bottom-right: row i's own key is 4 + i
+    assert np.allclose(o, v[own], rtol=0, atol=1e-15)
+    assert np.allclose(l, 0.5 * np.einsum("id,id->i", q, k[own]), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("window", [2, 5, 13])
+@pytest.mark.parametrize("causal", [True, False])
+def test_window_rows_equal_full_attention_over_their_key_range(window, causal):
+    g = np.random.default_rng(43 + window)
+    lq, lk = 9, 21
+    q, k, v = g.normal(size=(lq, 6)), g.normal(size=(lk, 6)), g.normal(size=(lk, 6))
+    o, l = oa.attend(q, k, v, 0.4, causal, window=window)
+    for i in range(lq):
+        lo = max(0, lk - lq + i - window + 1)
+        hi = (lk - lq + i + 1) if causal else lk
+        # brute force over the key range, written out
+        s = [0.4 * float(q[i] @ k[j]) for j in range(lo, hi)]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        ref = sum(wj * v[lo + n] for n, wj in enumerate(w)) / sum(w)
+        assert np.allclose(o[i], ref, rtol=0, atol=1e-12)
+        assert abs(l[i] - (m + math.log(sum(w)))) < 1e-12
+
+
+def test_window_decode_row_equals_last_prefill_row_and_paged_equals_contiguous():
+    g = np.random.default_rng(44)
+    lk, d, hkv, g_ = 50, 8, 2, 2
+    q = g.normal(size=(lk, hkv * g_, d))
+    k, v = g.normal(size=(lk, hkv, d)), g.normal(size=(lk, hkv, d))
+    o_p, l_p = oa.prefill_varlen(q, k, v, [0, lk], True, 0.25, window=7)
+    bs = 16
+    nblk = -(-lk // bs)
+    table = np.array([list(np.random.default_rng(1).permutation(nblk))])
+    kc = np.zeros((nblk, hkv, bs, d))
+    vc = np.zeros((nblk, hkv, d, bs))
+    for t in range(lk):
+        kc[table[0][t // bs], :, t % bs, :] = k[t]
+        vc[table[0][t // bs], :, :, t % bs] = v[t]
+    o_d, l_d = oa.decode_paged(q[-1:], kc, vc, table, [lk], 0.25, kv_format="f64", window=7)
+    assert np.allclose(o_d[0], o_p[-1], rtol=0, atol=1e-13) and np.allclose(l_d[0], l_p[-1], rtol=0, atol=1e-13)
