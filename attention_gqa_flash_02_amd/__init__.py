@@ -77,9 +77,9 @@ def _kv_dtype(cache):
 
 
 def attn_prefill_varlen(q, k, v, cu_seqlens, causal, scale, out=None, lse=None, max_seqlen=None,
-                        return_lse=True, stream=None):
-    """q [T, Hq, D], k/v [T, Hkv, D] bf16; cu_seqlens int32 [B+1] on the same device.
-    Returns (out [T, Hq, D] bf16, lse [T, Hq] fp32 or None)."""
+                        return_lse=True, stream=None, window=0):
+    """q [T, Hq, D], k/v [T, Hkv, D] bf16; cu_seqlens int32 [B+1] on the same device; window > 0 = a
+    sliding window of that many keys. Returns (out [T, Hq, D] bf16, lse [T, Hq] fp32 or None)."""
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check(t, name, torch.bfloat16, dev)
@@ -94,7 +94,7 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, causal, scale, out=None, lse=None, 
     if lse is None and return_lse:
         lse = torch.empty((total, hq), dtype=torch.float32, device=dev)
     st = _lib.load().attn_prefill_varlen(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), int(bool(causal)), float(scale), _ptr(out), _ptr(lse),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), int(bool(causal)), float(scale), int(window), _ptr(out), _ptr(lse),
         cu_seqlens.numel() - 1, total, int(max_seqlen), hq, hkv, d, _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_prefill_varlen")
@@ -126,7 +126,7 @@ def _workspace(nbytes, device, workspace):
 
 
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale=None, v_scale=None,
-                      out=None, lse=None, num_splits=0, workspace=None, return_lse=True, stream=None):
+                      out=None, lse=None, num_splits=0, workspace=None, return_lse=True, stream=None, window=0):
     """q [B, Hq, D] bf16; k_cache [N, Hkv, bs, D], v_cache [N, Hkv, D, bs] (bf16, or uint8 e4m3fn codes
     with k_scale/v_scale fp32 [Hkv]); block_table int32 [B, max_blocks]; seq_lens int32 [B]."""
     dev = q.device
@@ -153,7 +153,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale
         lse = torch.empty((b, hq), dtype=torch.float32, device=dev)
     st = _lib.load().attn_decode_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), kvt, _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
-        _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), b, hq, hkv, d, bs, nblk, maxblk, splits,
+        _ptr(seq_lens), float(scale), int(window), _ptr(out), _ptr(lse), b, hq, hkv, d, bs, nblk, maxblk, splits,
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_paged")
@@ -162,7 +162,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale
 
 def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k, causal, scale,
                       k_scale=None, v_scale=None, out=None, lse=None, max_q_len=None, num_splits=0,
-                      workspace=None, return_lse=True, stream=None):
+                      workspace=None, return_lse=True, stream=None, window=0):
     """Mixed varlen batch (prefill chunks over cached prefixes and decode tokens) over a paged cache."""
     dev = q.device
     _check(q, "q", torch.bfloat16, dev)
@@ -190,7 +190,7 @@ def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k
         lse = torch.empty((tq, hq), dtype=torch.float32, device=dev)
     st = _lib.load().attn_varlen_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), kvt, _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
-        _ptr(cu_seqlens_q), _ptr(seq_lens_k), int(bool(causal)), float(scale), _ptr(out), _ptr(lse),
+        _ptr(cu_seqlens_q), _ptr(seq_lens_k), int(bool(causal)), float(scale), int(window), _ptr(out), _ptr(lse),
         b, tq, int(max_q_len), hq, hkv, d, bs, nblk, maxblk, splits, _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     if st != 0:

@@ -66,13 +66,13 @@ const char* attn_status_string(attn_status status) {
 }
 
 attn_status attn_prefill_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
-                                int32_t causal, float scale, void* out, float* lse, int32_t num_seqs,
+                                int32_t causal, float scale, int32_t window, void* out, float* lse, int32_t num_seqs,
                                 int32_t total_tokens, int32_t max_seqlen, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim, void* stream) {
   if (!q || !k || !v || !cu_seqlens || !out) return ATTN_ERR_NULL;
   if (num_seqs <= 0 || total_tokens < 0 || max_seqlen < 0 || max_seqlen > total_tokens ||
       num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-      (causal != 0 && causal != 1) || !(std::isfinite(scale) && scale >= 0.f))
+      (causal != 0 && causal != 1) || !(std::isfinite(scale) && scale >= 0.f) || window < 0)
     return ATTN_ERR_SHAPE;
   if (head_dim != 128 && head_dim != 256) return ATTN_ERR_UNSUPPORTED;
   if ((long long)total_tokens * num_q_heads * head_dim > (long long)INT_MAX * 8) return ATTN_ERR_SHAPE;
@@ -86,6 +86,7 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v, con
   p.out = static_cast<bf16*>(out);
   p.lse = lse;
   p.scale = scale;
+  p.window = window;
   p.num_seqs = num_seqs;
   p.Hq = num_q_heads;
   p.Hkv = num_kv_heads;
@@ -140,7 +141,7 @@ static attn_status validate_paged(const void* q, const void* k_cache, const void
 
 attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
                               const float* k_scale, const float* v_scale, const int32_t* block_table,
-                              const int32_t* seq_lens, float scale, void* out, float* lse,
+                              const int32_t* seq_lens, float scale, int32_t window, void* out, float* lse,
                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
                               int32_t max_blocks_per_seq, int32_t num_splits, void* workspace,
@@ -149,7 +150,7 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
                                   out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                   num_blocks, max_blocks_per_seq, num_splits);
   if (st != ATTN_OK) return st;
-  if (!(std::isfinite(scale) && scale >= 0.f)) return ATTN_ERR_SHAPE;
+  if (!(std::isfinite(scale) && scale >= 0.f) || window < 0) return ATTN_ERR_SHAPE;
   const int g = num_q_heads / num_kv_heads;
   if (g > 16) return ATTN_ERR_UNSUPPORTED;
   const int S = attn_decode_num_splits(num_seqs, num_kv_heads, head_dim, kv_dtype, block_size,
@@ -172,6 +173,7 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   p.ws_lse = p.ws_o + (size_t)S * 2 * 16 * head_dim;
   p.ws_prefix = reinterpret_cast<int32_t*>(p.ws_lse + (size_t)S * 2 * 16);
   p.scale = scale;
+  p.window = window;
   p.num_seqs = num_seqs;
   p.Hq = num_q_heads;
   p.Hkv = num_kv_heads;
@@ -193,7 +195,7 @@ size_t attn_varlen_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32
 attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
                               const float* k_scale, const float* v_scale, const int32_t* block_table,
                               const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t causal,
-                              float scale, void* out, float* lse, int32_t num_seqs, int32_t total_q,
+                              float scale, int32_t window, void* out, float* lse, int32_t num_seqs, int32_t total_q,
                               int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                               int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
@@ -203,7 +205,7 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
   if (st != ATTN_OK) return st;
   if (!cu_seqlens_q) return ATTN_ERR_NULL;
   if (total_q < 0 || max_q_len < 0 || max_q_len > total_q || (causal != 0 && causal != 1) ||
-      !(std::isfinite(scale) && scale >= 0.f))
+      !(std::isfinite(scale) && scale >= 0.f) || window < 0)
     return ATTN_ERR_SHAPE;
   if ((long long)total_q * num_q_heads * head_dim > (long long)INT_MAX * 8) return ATTN_ERR_SHAPE;
   const int S = attn_decode_num_splits(num_seqs, num_kv_heads, head_dim, kv_dtype, block_size,
@@ -229,6 +231,7 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
   dp.ws_lse = dp.ws_o + (size_t)S * 2 * 16 * head_dim;
   dp.ws_prefix = reinterpret_cast<int32_t*>(dp.ws_lse + (size_t)S * 2 * 16);
   dp.scale = scale;
+  dp.window = window;
   dp.num_seqs = num_seqs;
   dp.Hq = num_q_heads;
   dp.Hkv = num_kv_heads;
@@ -250,6 +253,7 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
   pp.block_table = block_table;
   pp.seq_lens_k = seq_lens_k;
   pp.scale = scale;
+  pp.window = window;
   pp.num_seqs = num_seqs;
   pp.Hq = num_q_heads;
   pp.Hkv = num_kv_heads;

@@ -39,6 +39,7 @@
 //   * the four waves' (max, sum, O) are combined in LDS in a fixed order.
 #pragma once
 
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -63,16 +64,25 @@ struct PagedParams {
   int32_t* ws_prefix;          // [B + 1] chunk-count prefix sums, written by workgroup 0
   float scale;
   int num_seqs, Hq, Hkv, g, bs, max_blocks, num_wg, causal;
+  int window;                  // > 0: row i of a request also drops keys j < len - qlen + i - window + 1
 };
 
+// First key any row of a request with qlen new rows and len keys may see (the sliding window's
+// lower bound of its first row; 0 without a window).
+__device__ __forceinline__ int decode_key_begin(const PagedParams& p, int len, int qlen) {
+  return p.window > 0 ? max(0, len - qlen - p.window + 1) : 0;
+}
+
 // Chunk count of request b on this path (0 when its rows belong to another path or it has
-// no new rows): ceil(len / CH) chunks per kv head.
+// no new rows): the chunks from the first visible key to the last key, per kv head.
 template <int CH>
 __device__ __forceinline__ int decode_chunks(const PagedParams& p, int b) {
   const int len = p.seq_lens_k[b];
-  int rows = p.g;
-  if (p.cu_seqlens_q) rows = (p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b]) * p.g;
-  return (rows > 0 && rows <= 16) ? (len + CH - 1) / CH : 0;
+  const int qlen = p.cu_seqlens_q ? (p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b]) : 1;
+  const int rows = qlen * p.g;
+  if (!(rows > 0 && rows <= 16)) return 0;
+  // chunks from the one holding the first visible key (chunk indices of a unit count from there)
+  return (len + CH - 1) / CH - decode_key_begin(p, len, qlen) / CH;
 }
 
 // First chunk of workgroup g's share of T chunks: shares are whole groups of 4 chunks,
@@ -118,7 +128,8 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
   const int qlen = p.cu_seqlens_q ? (p.cu_seqlens_q[b + 1] - q0) : 1;
   const int R = qlen * p.g;
   const bool direct = slot < 0;
-  const int t_end = min(len, c1 * CH);
+  const int kc0 = decode_key_begin(p, len, qlen) / CH;   // chunk c of the unit is key chunk kc0 + c
+  const int t_end = min(len, (kc0 + c1) * CH);
 
   float kscale = 1.f, vscale = 1.f;
   if (KVT == KV_FP8) { kscale = p.k_scale[kvh]; vscale = p.v_scale[kvh]; }
@@ -128,10 +139,12 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
   // ---- Q^T operands (B of the QK MFMA): lane (j = row, qd) holds Q[row][d-slots].
   bf16x8 qB[KK];
   int limit;                                          // last visible key of row j
+  int lower;                                          // first visible key of row j
   {
     const int r = j;
     const int i = (r < R) ? r / p.g : 0;
     limit = p.causal ? (len - qlen + i) : (len - 1);
+    lower = p.window > 0 ? (len - qlen + i - p.window + 1) : INT_MIN;
     if (r < R) {
       const int h = kvh * p.g + (r % p.g);
       const bf16* qrow = p.q + ((size_t)(q0 + i) * p.Hq + h) * D;
@@ -170,6 +183,7 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
   const size_t block_stride = (size_t)p.Hkv * page_bytes;
   const int last_tok = len - 1;
   const int min_limit = p.causal ? (len - qlen) : (len - 1);   // smallest last-visible key of any row
+  const int max_lower = p.window > 0 ? (len - p.window) : INT_MIN;  // largest first-visible key of any row
 
   // Token layout of a chunk: in half h (32 tokens), lane quad q owns the 8-token run
   // T0 + 32h + 8q .. +7, and score slot s of sub-tile u = 2h + e is token T0 + 32h + 8q + 4e + s.
@@ -181,7 +195,7 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
   auto k_block = [&](int T0, int h) { return min(T0 + 32 * h + 8 * (j >> 2), last_tok) / p.bs; };
   auto v_block = [&](int T0, int h) { return min(T0 + 32 * h + 8 * qd, last_tok) / p.bs; };
 
-  int T0 = (c0 + wave_first) * CH;
+  int T0 = (kc0 + c0 + wave_first) * CH;
   int kphys[NH], vphys[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) kphys[h] = vphys[h] = 0;
@@ -251,16 +265,16 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
       st[u] = a * c;
     }
     // A chunk is a tail chunk when some row may not see all of its keys (the end of the request,
-    // or the causal edge of a multi-token request). Only tail chunks mask scores, zero V slots
+    // the causal edge of a multi-token request, or the start of a sliding window). Only tail chunks mask scores, zero V slots
     // past the end, and carry P as hi + lo bf16 parts: there rows see few keys, so the rounding
     // of P would not average out.
-    const bool tail = (T0 + CH - 1 > min_limit);
+    const bool tail = (T0 + CH - 1 > min_limit) || (T0 < max_lower);
     if (tail) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int tok0 = T0 + 32 * (u >> 1) + 8 * qd + 4 * (u & 1);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) st[u][s] = (tok0 + s <= limit) ? st[u][s] : kNegInf;
+        for (int s = 0; s < 4; ++s) st[u][s] = (tok0 + s <= limit && tok0 + s >= lower) ? st[u][s] : kNegInf;
       }
     }
     float mloc = kNegInf;

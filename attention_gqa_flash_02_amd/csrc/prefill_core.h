@@ -7,7 +7,9 @@
 // when the maximum moves) and accumulates P V. Only O and one log-sum-exp per
 // row are written; the score matrix never leaves the chip. Causal masking is
 // bottom-right aligned: row i of a request with Lq new rows and Lk keys sees
-// keys j <= Lk - Lq + i (for self-attention Lq = Lk).
+// keys j <= Lk - Lq + i (for self-attention Lq = Lk); a sliding window W also
+// drops keys j < Lk - Lq + i - W + 1 (a workgroup's loop starts at the tile
+// holding its first visible key; tiles below some row's lower bound mask it).
 //
 // Layout of the work:
 //   * a workgroup is 4 waves; each wave owns 32 query rows = 32 tokens of one
@@ -40,6 +42,8 @@
 //     folded into c and v_scale into the final normalisation).
 #pragma once
 
+#include <climits>
+
 #include "common.h"
 
 namespace attn {
@@ -66,6 +70,7 @@ struct PrefillParams {
   const int32_t* tile_prefix;  // [B + 1] prefix sums of q-tiles per request on this path
   float scale;
   int num_seqs, Hq, Hkv, g, hpw, causal, num_qtiles, bs, max_blocks;
+  int window;                  // > 0: row i also drops keys j < shift + i - window + 1
 };
 
 template <int D, int BN>
@@ -111,7 +116,8 @@ struct ContigLoader {
   int koff[K_LOADS], voff[4 * VB];
   int kch, krow0, vkg, vdc;
 
-  __device__ __forceinline__ void init(const PrefillParams& p, int b, int kvh, int Lk) {
+  __device__ __forceinline__ void init(const PrefillParams& p, int b, int kvh, int Lk, int first_tile) {
+    (void)first_tile;
     const int tid = threadIdx.x;
     const int seq0 = p.cu_seqlens_q[b];
     const long long stride = (long long)p.Hkv * D;
@@ -187,7 +193,7 @@ struct PagedLoader {
   size_t block_stride;                              // bytes between consecutive blocks
   int Lk, bs;
 
-  __device__ __forceinline__ void init(const PrefillParams& p, int b, int kvh, int Lk_) {
+  __device__ __forceinline__ void init(const PrefillParams& p, int b, int kvh, int Lk_, int first_tile) {
     const size_t page = (size_t)p.bs * D * ELT;
     kc = reinterpret_cast<const char*>(p.k_cache) + (size_t)kvh * page;
     vc = reinterpret_cast<const char*>(p.v_cache) + (size_t)kvh * page;
@@ -195,7 +201,7 @@ struct PagedLoader {
     table = p.block_table + (size_t)b * p.max_blocks;
     Lk = Lk_;
     bs = p.bs;
-    if (Lk > 0) load_table(0);
+    if (first_tile * BN < Lk) load_table(first_tile);
   }
   // Block-table entries are loaded one tile ahead of the K/V loads that use them, so a fetch
   // never waits on a table load.
@@ -316,6 +322,13 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
   const int kv_end = p.causal ? min(Lk, shift + min(Lq, t0 + TQ)) : Lk;
   const int wave_kv_end = p.causal ? min(Lk, shift + min(Lq, tw + 32)) : Lk;
   const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  // sliding window: the first key any row of the workgroup / of this wave sees, and the largest
+  // first-visible key of the wave's rows (tiles below it mask the lower edge)
+  const int win = p.window;
+  const int kv_begin = win > 0 ? max(0, shift + t0 - win + 1) : 0;
+  const int wave_kv_begin = win > 0 ? max(0, shift + tw - win + 1) : 0;
+  const int wave_lower_max = win > 0 ? shift + tw + 31 - win + 1 : INT_MIN;
+  const int n_first = min(kv_begin / BN, ntiles);
   float kscale = 1.f, vscale = 1.f;
   if (PAGED && p.k_scale) { kscale = p.k_scale[kvh]; vscale = p.v_scale[kvh]; }
   const float c = p.scale * kscale * kLog2e;
@@ -338,6 +351,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
   for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qB[kk]));
   // last key row j may see, and the first key at which some row of the wave stops seeing keys
   const int lim = p.causal ? min(shift + qrow_i, Lk - 1) : (Lk - 1);
+  const int lower = win > 0 ? shift + qrow_i - win + 1 : INT_MIN;   // first key row j may see
   // first key that some row of the wave does not see (tiles reaching it need the mask)
   const int wave_mask_from = p.causal ? max(0, shift + tw + 1) : Lk;
 
@@ -349,19 +363,20 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
   float mc = kNegInf, l = 0.f;
 
   Loader ld;
-  ld.init(p, b, kvh, Lk);
-  if (ntiles > 0) {
-    ld.fetch(0);
-    ld.stage(smem, smem + S::K_ELEMS);
+  ld.init(p, b, kvh, Lk, n_first);
+  if (n_first < ntiles) {
+    ld.fetch(n_first);
+    bf16* nb = smem + (n_first & 1) * S::BUF;
+    ld.stage(nb, nb + S::K_ELEMS);
   }
   __syncthreads();
   const int kperm = key_perm32(j);
 
-  for (int n = 0; n < ntiles; ++n) {
+  for (int n = n_first; n < ntiles; ++n) {
     const int cur = n & 1;
     if (n + 1 < ntiles) ld.fetch(n + 1);
     const int n0 = n * BN;
-    if (wave_active && n0 < wave_kv_end) {
+    if (wave_active && n0 < wave_kv_end && n0 + BN > wave_kv_begin) {
       const bf16* Ks = smem + cur * S::BUF;
       const bf16* Vt = Ks + S::K_ELEMS;
       // S^T = K . Q^T
@@ -376,14 +391,14 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
           st[kb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(krow + 16 * kk), qB[kk], st[kb]);
       }
       // tiles that cross the causal edge of some row of the wave or the end of the keys
-      const bool edge = (n0 + BN > Lk) || (n0 + BN - 1 >= wave_mask_from);
+      const bool edge = (n0 + BN > Lk) || (n0 + BN - 1 >= wave_mask_from) || (n0 < wave_lower_max);
       if (edge) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = n0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
-            st[kb][r] = (key <= lim) ? st[kb][r] : kNegInf;
+            st[kb][r] = (key <= lim && key >= lower) ? st[kb][r] : kNegInf;
           }
       }
       // tile maximum of the raw scores (c >= 0, so it maps to the maximum of t = c * s)

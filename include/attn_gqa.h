@@ -38,6 +38,12 @@
  *     num_kv_heads; block_size must be 16, 32, 64, 128 or 256; paged calls
  *     take at most 16384 requests.
  *   - scale (every call) must be finite and >= 0; otherwise ATTN_ERR_SHAPE.
+ *   - window (every attention call): 0 = no window; W > 0 = sliding window:
+ *     row i additionally drops the keys j < Lk - Lq + i - W + 1, so with causal
+ *     masking it sees its own position and the W - 1 keys before it (a lower
+ *     bound on the visible keys, bottom-right aligned like the causal bound;
+ *     "Optimization 1", section 2 on shrinking the KV a token attends to; the
+ *     NVIDIA guideline summary, principle 3). Negative: ATTN_ERR_SHAPE.
  *   - stream is a hipStream_t (NULL = the default stream). Calls return once
  *     the work is enqueued; results are valid after the stream synchronises.
  *   - Argument validation is synchronous and happens before anything is
@@ -86,7 +92,7 @@ const char* attn_status_string(attn_status status);
  * Needs no workspace: nothing but out and lse is written.
  */
 attn_status attn_prefill_varlen(const void* q, const void* k, const void* v,
-                                const int32_t* cu_seqlens, int32_t causal, float scale,
+                                const int32_t* cu_seqlens, int32_t causal, float scale, int32_t window,
                                 void* out, float* lse,
                                 int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -140,7 +146,7 @@ size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32
  */
 attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                               int32_t kv_dtype, const float* k_scale, const float* v_scale,
-                              const int32_t* block_table, const int32_t* seq_lens, float scale,
+                              const int32_t* block_table, const int32_t* seq_lens, float scale, int32_t window,
                               void* out, float* lse,
                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
@@ -166,7 +172,7 @@ size_t attn_varlen_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32
 attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_cache,
                               int32_t kv_dtype, const float* k_scale, const float* v_scale,
                               const int32_t* block_table, const int32_t* cu_seqlens_q,
-                              const int32_t* seq_lens_k, int32_t causal, float scale,
+                              const int32_t* seq_lens_k, int32_t causal, float scale, int32_t window,
                               void* out, float* lse,
                               int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -25,19 +25,19 @@ def cache_np(t):
     return t.view(torch.uint8).numpy()
 
 
-def oracle_prefill(case, units=None):
+def oracle_prefill(case, units=None, window=0):
     return oracle.prefill_varlen(bf16_np(case.q), bf16_np(case.k), bf16_np(case.v),
-                                 case.cu_seqlens.cpu().numpy(), case.causal, case.scale, units=units)
+                                 case.cu_seqlens.cpu().numpy(), case.causal, case.scale, units=units, window=window)
 
 
-def oracle_paged(case, units=None):
+def oracle_paged(case, units=None, window=0):
     fmt = "bf16" if case.kv_format == "bf16" else "e4m3fn"
     ks = None if case.k_scale is None else case.k_scale.cpu().numpy().astype(np.float64)
     vs = None if case.v_scale is None else case.v_scale.cpu().numpy().astype(np.float64)
     return oracle.varlen_paged(bf16_np(case.q), cache_np(case.k_cache), cache_np(case.v_cache),
                                case.block_table.cpu().numpy(), case.cu_seqlens_q.cpu().numpy(),
                                case.seq_lens_k.cpu().numpy(), case.causal, case.scale,
-                               kv_format=fmt, k_scale=ks, v_scale=vs, units=units)
+                               kv_format=fmt, k_scale=ks, v_scale=vs, units=units, window=window)
 
 
 def compare(out, lse, ref_out, ref_lse, max_abs=MAX_ABS, mean_abs=MEAN_ABS, lse_abs=LSE_ABS, label=""):

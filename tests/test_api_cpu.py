@@ -34,18 +34,19 @@ def test_status_strings():
 
 
 def _prefill(**kw):
-    args = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, causal=1, scale=0.1, out=FAKE, lse=None, nseq=1, total=16,
-                maxlen=16, hq=4, hkv=1, d=128)
+    args = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, causal=1, scale=0.1, window=0, out=FAKE, lse=None, nseq=1,
+                total=16, maxlen=16, hq=4, hkv=1, d=128)
     args.update(kw)
     return _lib.load().attn_prefill_varlen(args["q"], args["k"], args["v"], args["cu"], args["causal"],
-                                           args["scale"], args["out"], args["lse"], args["nseq"], args["total"],
+                                           args["scale"], args["window"], args["out"], args["lse"], args["nseq"],
+                                           args["total"],
                                            args["maxlen"], args["hq"], args["hkv"], args["d"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(cu=None), 1), (dict(out=None), 1),
     (dict(nseq=0), 2), (dict(hq=6, hkv=4), 2), (dict(hkv=0), 2), (dict(total=-1), 2), (dict(maxlen=17), 2),
-    (dict(causal=2), 2), (dict(scale=float("nan")), 2), (dict(scale=-0.5), 2),
+    (dict(causal=2), 2), (dict(scale=float("nan")), 2), (dict(scale=-0.5), 2), (dict(window=-1), 2),
     (dict(d=64), 3), (dict(d=192), 3),
 ])
 def test_prefill_validation(kw, code):
@@ -57,11 +58,12 @@ def test_prefill_empty_batch_is_a_noop():
 
 
 def _decode(**kw):
-    a = dict(q=FAKE, kc=FAKE, vc=FAKE, kvt=0, ks=None, vs=None, table=FAKE, lens=FAKE, scale=0.1, out=FAKE,
-             lse=None, nseq=2, hq=8, hkv=2, d=128, bs=16, nblk=10, maxblk=4, splits=1, ws=None, wsb=0)
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, kvt=0, ks=None, vs=None, table=FAKE, lens=FAKE, scale=0.1, window=0,
+             out=FAKE, lse=None, nseq=2, hq=8, hkv=2, d=128, bs=16, nblk=10, maxblk=4, splits=1, ws=None, wsb=0)
     a.update(kw)
     return _lib.load().attn_decode_paged(a["q"], a["kc"], a["vc"], a["kvt"], a["ks"], a["vs"], a["table"],
-                                         a["lens"], a["scale"], a["out"], a["lse"], a["nseq"], a["hq"], a["hkv"],
+                                         a["lens"], a["scale"], a["window"], a["out"], a["lse"], a["nseq"], a["hq"],
+                                         a["hkv"],
                                          a["d"], a["bs"], a["nblk"], a["maxblk"], a["splits"], a["ws"], a["wsb"],
                                          None)
 
@@ -71,6 +73,7 @@ def _decode(**kw):
     (dict(kvt=1), 1),                               # fp8 without scales
     (dict(kvt=7), 3), (dict(d=96), 3), (dict(bs=8), 3), (dict(bs=48), 3), (dict(hq=64, hkv=2), 3),
     (dict(nseq=-1), 2), (dict(nseq=16385), 3), (dict(hq=7), 2), (dict(nblk=0), 2), (dict(maxblk=0), 2), (dict(splits=-2), 2),
+    (dict(window=-3), 2),
     (dict(splits=2, maxblk=40), 4),                 # partials need a workspace
     (dict(splits=2, maxblk=40, ws=FAKE, wsb=16), 4),
 ])
@@ -96,12 +99,15 @@ def test_split_planning_and_workspace_sizes():
 
 def test_varlen_validation():
     lib = _lib.load()
-    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, None, FAKE, 1, 0.1, FAKE, None,
+    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, None, FAKE, 1, 0.1, 0, FAKE, None,
                                2, 10, 5, 8, 2, 128, 16, 10, 4, 1, None, 0, None)
     assert st == 1                                   # cu_seqlens_q missing
-    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None,
+    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, 0, FAKE, None,
                                2, 10, 11, 8, 2, 128, 16, 10, 4, 1, None, 0, None)
     assert st == 2                                   # max_q_len > total_q
+    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, -1, FAKE, None,
+                               2, 10, 5, 8, 2, 128, 16, 10, 4, 1, None, 0, None)
+    assert st == 2                                   # negative window
 
 
 def _append(**kw):
