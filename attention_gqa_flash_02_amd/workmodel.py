@@ -17,20 +17,21 @@ padding, softmax arithmetic and re-reads are not counted.
 import numpy as np
 
 
-def visible_pairs(q_len, kv_len, causal):
+def visible_pairs(q_len, kv_len, causal, window=0):
     """Number of (row, key) pairs a request's rows see: row i of q_len rows over
-    kv_len keys sees clip(kv_len - q_len + i + 1, 0, kv_len) keys when causal
-    (bottom-right alignment), all kv_len otherwise."""
+    kv_len keys sees keys [lo_i, hi_i] with hi_i = kv_len - q_len + i when causal
+    (bottom-right alignment, else kv_len - 1) and lo_i = kv_len - q_len + i - window + 1
+    with a sliding window (else 0), both clipped to [0, kv_len - 1]."""
     q_len, kv_len = int(q_len), int(kv_len)
-    if not causal:
-        return q_len * kv_len
     rows = np.arange(q_len, dtype=np.int64)
-    return int(np.clip(kv_len - q_len + rows + 1, 0, kv_len).sum())
+    hi = np.clip(kv_len - q_len + rows, -1, kv_len - 1) if causal else np.full(q_len, kv_len - 1)
+    lo = np.clip(kv_len - q_len + rows - window + 1, 0, kv_len) if window > 0 else np.zeros(q_len, dtype=np.int64)
+    return int(np.maximum(hi - lo + 1, 0).sum())
 
 
-def prefill_flops(q_lens, kv_lens, num_q_heads, head_dim, causal=True):
+def prefill_flops(q_lens, kv_lens, num_q_heads, head_dim, causal=True, window=0):
     """4 * D * Hq * sum of visible pairs over requests."""
-    pairs = sum(visible_pairs(a, b, causal) for a, b in zip(q_lens, kv_lens))
+    pairs = sum(visible_pairs(a, b, causal, window) for a, b in zip(q_lens, kv_lens))
     return 4 * int(head_dim) * int(num_q_heads) * pairs
 
 

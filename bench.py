@@ -137,19 +137,19 @@ def decode_section(lib, case, splits, steps, warmup, label):
             "kernel_ms_median": statistics.median(durs), "kernel_ms_min": min(durs), "out": out, "lse": lse}
 
 
-def prefill_section(lib, case, steps, warmup):
+def prefill_section(lib, case, steps, warmup, window=0):
     from attention_gqa_flash_02_amd import workmodel
-    flops = workmodel.prefill_flops(case.seqlens, case.seqlens, case.num_q_heads, case.head_dim, case.causal)
+    flops = workmodel.prefill_flops(case.seqlens, case.seqlens, case.num_q_heads, case.head_dim, case.causal, window)
     out, lse = lib.attn_prefill_varlen(case.q, case.k, case.v, case.cu_seqlens, case.causal, case.scale,
-                                       max_seqlen=case.max_seqlen)
+                                       max_seqlen=case.max_seqlen, window=window)
 
     def call():
         lib.attn_prefill_varlen(case.q, case.k, case.v, case.cu_seqlens, case.causal, case.scale, out=out,
-                                lse=lse, max_seqlen=case.max_seqlen)
+                                lse=lse, max_seqlen=case.max_seqlen, window=window)
     wall, durs = time_steps([call], steps, warmup)
     kern = statistics.mean(durs)
-    log(f"[bench] prefill: wall/step={wall:.4f} ms kernel mean={kern:.4f} min={min(durs):.4f} ms -> "
-        f"{flops / kern / 1e9:.1f} TFLOP/s")
+    log(f"[bench] prefill{f' window={window}' if window else ''}: wall/step={wall:.4f} ms kernel mean={kern:.4f} "
+        f"min={min(durs):.4f} ms -> {flops / kern / 1e9:.1f} TFLOP/s")
     return {"flops": flops, "wall_ms": wall, "kernel_ms_mean": kern, "kernel_ms_min": min(durs), "out": out,
             "lse": lse}
 
@@ -351,7 +351,15 @@ def main():
             par = sampled_parity_prefill(c3, pre["out"], pre["lse"], units)
             log(f"[bench] prefill parity on {units}: {par}")
             extra["prefill_c3"]["parity_sample"] = par
-        del c3, pre
+        pw = prefill_section(lib, c3, max(5, a.steps // 5), max(2, a.warmup // 2), window=4096)
+        tfw = pw["flops"] / pw["kernel_ms_mean"] / 1e9
+        extra["prefill_c3_window4096"] = {
+            "workload": "the same causal prefill with a 4096-key sliding window (algorithmic FLOPs over the "
+                        "windowed visible pairs)",
+            "tflops": tfw, "ms": pw["kernel_ms_mean"], "algorithmic_flops": pw["flops"],
+            "roofline": {"bound": "mfma", "achieved": tfw, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": tfw / MFMA_BF16_PEAK_TFS, "traffic": None}}
+        del c3, pre, pw
         torch.cuda.empty_cache()
 
     if run("c4"):

@@ -49,3 +49,18 @@ def test_visible_pairs_bruteforce(lq, lk):
 def test_c3_flops():
     assert wm.prefill_flops([8192] * 4, [8192] * 4, 32, 128) == 4 * 128 * 32 * 4 * (8192 * 8193 // 2)
     assert wm.prefill_flops([8192] * 4, [8192] * 4, 32, 128) == 2_199_291_691_008
+
+
+@pytest.mark.parametrize("lq,lk,w", [(5, 5, 1), (5, 5, 3), (3, 10, 4), (10, 3, 2), (64, 200, 17), (8192, 8192, 4096)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_visible_pairs_with_window_bruteforce(lq, lk, w, causal):
+    pairs = 0
+    for i in range(min(lq, 300)):
+        for j in range(lk):
+            hi_ok = (j <= lk - lq + i) if causal else True
+            if hi_ok and j >= lk - lq + i - w + 1:
+                pairs += 1
+    if lq <= 300:
+        assert wm.visible_pairs(lq, lk, causal, w) == pairs
+    else:   # closed form for the long causal self-attention case: sum over rows of min(i + 1, w)
+        assert causal is False or wm.visible_pairs(lq, lk, causal, w) == sum(min(i + 1, w) for i in range(lq))
