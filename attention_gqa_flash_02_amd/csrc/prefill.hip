@@ -1,10 +1,11 @@
 // Prefill and mixed-batch kernel instantiations and launchers.
 #include "launch.h"
+#include "prefill_pp.h"
 
 namespace attn {
 
-// Varlen self-attention over contiguous K/V. Grid: (head groups, requests, q-tiles), q-tiles
-// walked heaviest (last) first.
+// Varlen self-attention over contiguous K/V with head_dim 256 (head_dim 128 takes the ping-pong
+// kernel below). Grid: (head groups, requests, q-tiles), q-tiles walked heaviest (last) first.
 // Two workgroups per compute unit (two waves per SIMD, so one wave's softmax overlaps the
 // other's MFMAs) when the head dimension leaves room in the register file.
 template <int D>
@@ -16,6 +17,15 @@ void prefill_varlen_kernel(PrefillParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   prefill_tile_body<D, BN, ContigLoader<D, BN>, false>(p, reinterpret_cast<bf16*>(smem_raw), blockIdx.x,
                                                         blockIdx.y, p.num_qtiles - 1 - (int)blockIdx.z);
+}
+
+// Varlen self-attention over contiguous K/V with head_dim 128: the ping-pong kernel (8 waves,
+// 64 KB of LDS, one workgroup per compute unit). Grid as above; a q-tile is 32 * 8 / hpw rows.
+template <int BN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_pingpong_kernel(PrefillParams p) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  prefill_pingpong_body<BN>(p, smem_raw, blockIdx.x, blockIdx.y, p.num_qtiles - 1 - (int)blockIdx.z);
 }
 
 // Q-tiles of request b on the prefill path of a mixed batch (its rows do not fit the decode path).
@@ -75,8 +85,27 @@ static hipError_t launch_prefill_t(const PrefillParams& p, int max_seqlen, hipSt
   return hipGetLastError();
 }
 
+template <int BN>
+static hipError_t launch_pingpong_t(const PrefillParams& p, int max_seqlen, hipStream_t stream) {
+  using S = PingPongShape<BN>;
+  static bool attr_set = false;  // per process; the attribute is a property of the function
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pingpong_kernel<BN>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tq = 32 * (8 / p.hpw);
+  PrefillParams q = p;
+  q.num_qtiles = (max_seqlen + tq - 1) / tq;
+  if (q.num_qtiles <= 0) return hipSuccess;
+  dim3 grid(p.Hkv * (p.g / p.hpw), p.num_seqs, q.num_qtiles);
+  hipLaunchKernelGGL((prefill_pingpong_kernel<BN>), grid, dim3(512), S::LDS_BYTES, stream, q);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, hipStream_t stream) {
-  if (head_dim == 128) return launch_prefill_t<128, 64>(p, max_seqlen, stream);
+  if (head_dim == 128) return launch_pingpong_t<64>(p, max_seqlen, stream);
   if (head_dim == 256) return launch_prefill_t<256, 64>(p, max_seqlen, stream);
   return hipErrorInvalidValue;
 }
