@@ -344,7 +344,7 @@ def main():
             "tflops": tf, "ms": pre["kernel_ms_mean"], "wall_ms": pre["wall_ms"],
             "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tf / MFMA_BF16_PEAK_TFS,
-                         "traffic": measured_traffic("prefill_c3", ["common.h", "prefill_core.h", "prefill.hip"])},
+                         "traffic": measured_traffic("prefill_c3", ["common.h", "prefill_core.h", "prefill_pp.h", "prefill.hip"])},
             "algorithmic_flops": pre["flops"]}
         if not a.quick:
             units = [(0, 0), (1, 7), (2, 19), (3, 31)]
@@ -399,7 +399,7 @@ def main():
             "prefill_kv_bytes": mx["prefill_kv_bytes"],
             "roofline": {"bound": "mfma", "lower_bound_ms": mx["t_star_ms"], "frac": mx["t_star_ms"] / mx["ms"],
                          "traffic": measured_traffic("mixed_c5", ["common.h", "decode_core.h", "decode.hip",
-                                                                  "prefill_core.h", "prefill.hip"])}}
+                                                                  "prefill_core.h", "prefill_pp.h", "prefill.hip"])}}
         if not a.quick:
             n_pre = sum(1 for ql in c5.q_lens if ql > 1)
             units = [(0, 0), (n_pre - 1, 15), (n_pre, 3), (n_pre + 50, 9), (len(c5.q_lens) - 1, 12)]

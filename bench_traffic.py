@@ -32,10 +32,10 @@ COPY_REPS = 8
 CASES = {
     "decode_paged_c2": (["decode_share_kernel", "decode_merge_kernel"], ["common.h", "decode_core.h", "decode.hip"]),
     "decode_c4": (["decode_share_kernel", "decode_merge_kernel"], ["common.h", "decode_core.h", "decode.hip"]),
-    "prefill_c3": (["prefill_varlen_kernel"], ["common.h", "prefill_core.h", "prefill.hip"]),
+    "prefill_c3": (["prefill_pingpong_kernel"], ["common.h", "prefill_core.h", "prefill_pp.h", "prefill.hip"]),
     "append_c5": (["kv_append_kernel"], ["append.hip"]),
     "mixed_c5": (["varlen_mixed_kernel", "decode_merge_kernel"],
-                 ["common.h", "decode_core.h", "decode.hip", "prefill_core.h", "prefill.hip"]),
+                 ["common.h", "decode_core.h", "decode.hip", "prefill_core.h", "prefill_pp.h", "prefill.hip"]),
 }
 
 
