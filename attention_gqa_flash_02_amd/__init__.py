@@ -20,6 +20,7 @@ __all__ = [
     "ATTN_KV_FP8_E4M3FN",
     "attn_status_string",
     "attn_prefill_varlen",
+    "attn_prefill_varlen_fp8",
     "attn_decode_num_splits",
     "attn_decode_workspace_bytes",
     "attn_decode_paged",
@@ -98,6 +99,39 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, causal, scale, out=None, lse=None, 
         cu_seqlens.numel() - 1, total, int(max_seqlen), hq, hkv, d, _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_prefill_varlen")
+    return out, lse
+
+
+def attn_prefill_varlen_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens, causal, scale, out=None, lse=None,
+                            max_seqlen=None, return_lse=True, stream=None, window=0):
+    """q [T, Hq, 128], k/v [T, Hkv, 128] e4m3fn codes (torch.uint8 or torch.float8_e4m3fn); q_scale [Hq],
+    k_scale/v_scale [Hkv] fp32; cu_seqlens int32 [B+1]; all on one device. Returns (out [T, Hq, 128] bf16,
+    lse [T, Hq] fp32 or None)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{name} must hold e4m3fn codes (uint8 or float8_e4m3fn), got {t.dtype}")
+        _check(t, name, t.dtype, dev)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check(t, name, torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    if q_scale.numel() != hq or k_scale.numel() != hkv or v_scale.numel() != hkv:
+        raise ValueError("q_scale needs num_q_heads entries, k_scale and v_scale num_kv_heads")
+    if max_seqlen is None:
+        cu = cu_seqlens.cpu()
+        max_seqlen = int((cu[1:] - cu[:-1]).max()) if cu.numel() > 1 else 0
+    if out is None:
+        out = torch.empty((total, hq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((total, hq), dtype=torch.float32, device=dev)
+    st = _lib.load().attn_prefill_varlen_fp8(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(cu_seqlens),
+        int(bool(causal)), float(scale), int(window), _ptr(out), _ptr(lse),
+        cu_seqlens.numel() - 1, total, int(max_seqlen), hq, hkv, d, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_prefill_varlen_fp8")
     return out, lse
 
 

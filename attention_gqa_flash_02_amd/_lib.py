@@ -18,6 +18,9 @@ SIGNATURES = {
     "attn_status_string": (ctypes.c_char_p, [c_i32]),
     "attn_prefill_varlen": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_f32, c_i32, c_void_p, c_void_p,
                                     c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_void_p]),
+    "attn_prefill_varlen_fp8": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_i32, c_f32, c_i32, c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32,
+                                        c_i32, c_i32, c_void_p]),
     "attn_decode_num_splits": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "attn_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32]),
     "attn_decode_paged": (c_i32, [c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -6,6 +6,7 @@
 
 #include "../../include/attn_gqa.h"
 #include "launch.h"
+#include "prefill_fp8.h"
 
 namespace attn {
 
@@ -69,14 +70,14 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v, con
                                 int32_t causal, float scale, int32_t window, void* out, float* lse, int32_t num_seqs,
                                 int32_t total_tokens, int32_t max_seqlen, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim, void* stream) {
-  if (!q || !k || !v || !cu_seqlens || !out) return ATTN_ERR_NULL;
   if (num_seqs <= 0 || total_tokens < 0 || max_seqlen < 0 || max_seqlen > total_tokens ||
       num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
       (causal != 0 && causal != 1) || !(std::isfinite(scale) && scale >= 0.f) || window < 0)
     return ATTN_ERR_SHAPE;
   if (head_dim != 128 && head_dim != 256) return ATTN_ERR_UNSUPPORTED;
   if ((long long)total_tokens * num_q_heads * head_dim > (long long)INT_MAX * 8) return ATTN_ERR_SHAPE;
-  if (total_tokens == 0 || max_seqlen == 0) return ATTN_OK;
+  if (total_tokens == 0 || max_seqlen == 0) return ATTN_OK;   // nothing to read or write
+  if (!q || !k || !v || !cu_seqlens || !out) return ATTN_ERR_NULL;
 
   PrefillParams p{};
   p.q = static_cast<const bf16*>(q);
@@ -94,6 +95,42 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v, con
   p.hpw = gcd_int(p.g, 4);
   p.causal = causal;
   hipError_t e = launch_prefill(p, head_dim, max_seqlen, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status attn_prefill_varlen_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                                    const float* k_scale, const float* v_scale, const int32_t* cu_seqlens,
+                                    int32_t causal, float scale, int32_t window, void* out, float* lse,
+                                    int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, void* stream) {
+  if (num_seqs <= 0 || total_tokens < 0 || max_seqlen < 0 || max_seqlen > total_tokens ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      (causal != 0 && causal != 1) || !(std::isfinite(scale) && scale >= 0.f) || window < 0)
+    return ATTN_ERR_SHAPE;
+  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)total_tokens * num_q_heads * head_dim > (long long)INT_MAX * 8) return ATTN_ERR_SHAPE;
+  if (total_tokens == 0 || max_seqlen == 0) return ATTN_OK;   // nothing to read or write
+  if (!q || !k || !v || !q_scale || !k_scale || !v_scale || !cu_seqlens || !out) return ATTN_ERR_NULL;
+
+  PrefillFp8Params p{};
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.out = static_cast<bf16*>(out);
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.scale = scale;
+  p.window = window;
+  p.num_seqs = num_seqs;
+  p.Hq = num_q_heads;
+  p.Hkv = num_kv_heads;
+  p.g = num_q_heads / num_kv_heads;
+  p.hpw = gcd_int(p.g, 4);
+  p.causal = causal;
+  hipError_t e = launch_prefill_fp8(p, max_seqlen, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -14,6 +14,11 @@ namespace attn {
 // walked heaviest (last) first.
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, hipStream_t stream);
 
+// FP8 varlen prefill over contiguous e4m3fn Q/K/V with per-head scales, head_dim 128 (the
+// parameter block is defined in prefill_fp8.h). Grid as launch_prefill's.
+struct PrefillFp8Params;
+hipError_t launch_prefill_fp8(const PrefillFp8Params& p, int max_seqlen, hipStream_t stream);
+
 // Split-KV paged decode: p.num_wg partition workgroups, each taking an equal share of the batch's
 // (request, kv head, key chunk) work, then the LSE merge (grid: rows x kv heads x requests).
 // rows_max = rows per (request, kv head) (<= 16); it sizes the LDS combine buffer and the merge

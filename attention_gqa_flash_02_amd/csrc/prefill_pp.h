@@ -314,9 +314,6 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
       }
       pedge = edge;
   };
-  // group A runs slots 2m (matrix) and 2m+1 (softmax) in iteration m and issues every tile load
-  // (in slot 2m, waited for at the end of slot 2m+1); group B, one slot later, runs slots 2m+1
-  // (matrix) and 2m+2 (softmax)
   // Group A runs slots 2m (matrix) and 2m+1 (softmax) in iteration m; group B, one slot later,
   // runs slots 2m+1 (matrix) and 2m+2 (softmax), and it issues the tile loads of every even slot 2j
   // (K j+1 and V j) at its start and waits for them at the end of slot 2j+1. The matrix work runs

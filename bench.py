@@ -14,7 +14,7 @@ roofline, checks sampled
 outputs against the fp64 oracle, and times the oracle itself on the host cores
 (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c2|c3|c4|c5|append]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c2|c3|c3fp8|c4|c5|append]
                        [--no-cpu-baseline] [--quick]
 Prints one JSON line.
 """
@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 4096 flop/clk x 2.4 GHz)
+MFMA_FP8_PEAK_TFS = 5033.2     # MI355X dense fp8 MFMA, TFLOP/s (twice the bf16 rate)
 CSRC = os.path.join(ROOT, "attention_gqa_flash_02_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -47,7 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--splits", type=int, default=0, help="decode partitions (0 = library choice)")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "append"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c3fp8", "c4", "c5", "append"], default=None,
                     help="time one workload only (for profiling); the JSON line still names c2's metric")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the parity samples")
@@ -150,6 +151,24 @@ def prefill_section(lib, case, steps, warmup, window=0):
     kern = statistics.mean(durs)
     log(f"[bench] prefill{f' window={window}' if window else ''}: wall/step={wall:.4f} ms kernel mean={kern:.4f} "
         f"min={min(durs):.4f} ms -> {flops / kern / 1e9:.1f} TFLOP/s")
+    return {"flops": flops, "wall_ms": wall, "kernel_ms_mean": kern, "kernel_ms_min": min(durs), "out": out,
+            "lse": lse}
+
+
+def prefill_fp8_section(lib, case, steps, warmup):
+    from attention_gqa_flash_02_amd import workmodel
+    flops = workmodel.prefill_flops(case.seqlens, case.seqlens, case.num_q_heads, case.head_dim, case.causal)
+    mx = max(case.seqlens)
+    out, lse = lib.attn_prefill_varlen_fp8(case.q, case.k, case.v, case.q_scale, case.k_scale, case.v_scale,
+                                           case.cu_seqlens, case.causal, case.scale, max_seqlen=mx)
+
+    def call():
+        lib.attn_prefill_varlen_fp8(case.q, case.k, case.v, case.q_scale, case.k_scale, case.v_scale,
+                                    case.cu_seqlens, case.causal, case.scale, out=out, lse=lse, max_seqlen=mx)
+    wall, durs = time_steps([call], steps, warmup)
+    kern = statistics.mean(durs)
+    log(f"[bench] prefill fp8: wall/step={wall:.4f} ms kernel mean={kern:.4f} min={min(durs):.4f} ms -> "
+        f"{flops / kern / 1e9:.1f} TFLOP/s")
     return {"flops": flops, "wall_ms": wall, "kernel_ms_mean": kern, "kernel_ms_min": min(durs), "out": out,
             "lse": lse}
 
@@ -271,6 +290,15 @@ def sampled_parity_paged(case, out, lse, units):
     return r
 
 
+def sampled_parity_prefill_fp8(case, out, lse, units):
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import oracle_prefill_fp8
+    ref_o, ref_l = oracle_prefill_fp8(case, units=units)
+    r = parity_stats(out, lse, ref_o, ref_l)
+    r["units"] = len(units)
+    return r
+
+
 def sampled_parity_prefill(case, out, lse, units):
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from helpers import oracle_prefill
@@ -360,6 +388,26 @@ def main():
             "roofline": {"bound": "mfma", "achieved": tfw, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tfw / MFMA_BF16_PEAK_TFS, "traffic": None}}
         del c3, pre, pw
+        torch.cuda.empty_cache()
+
+    if run("c3fp8"):
+        c3f = synth.make_prefill_fp8(3, [8192] * 4, 32, 8, 128, device=dev)
+        pf = prefill_fp8_section(lib, c3f, max(5, a.steps // 5), max(2, a.warmup // 2))
+        tf8 = pf["flops"] / pf["kernel_ms_mean"] / 1e9
+        extra["prefill_c3_fp8"] = {
+            "workload": "the same causal prefill with e4m3fn Q/K/V and per-head scales (N(0,1) draws, scale = "
+                        "amax/448 per head), fp8 MFMA, P rounded to e4m3, out bf16 + LSE",
+            "tflops": tf8, "ms": pf["kernel_ms_mean"], "wall_ms": pf["wall_ms"], "algorithmic_flops": pf["flops"],
+            "roofline": {"bound": "mfma", "achieved": tf8, "peak": MFMA_FP8_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": tf8 / MFMA_FP8_PEAK_TFS,
+                         "traffic": measured_traffic("prefill_c3_fp8", ["common.h", "prefill_core.h", "prefill_pp.h",
+                                                                        "prefill_fp8.h", "prefill_fp8.hip"])}}
+        if not a.quick:
+            units = [(0, 0), (1, 7), (2, 19), (3, 31)]
+            par = sampled_parity_prefill_fp8(c3f, pf["out"], pf["lse"], units)
+            log(f"[bench] prefill fp8 parity on {units}: {par}")
+            extra["prefill_c3_fp8"]["parity_sample"] = par
+        del c3f, pf
         torch.cuda.empty_cache()
 
     if run("c4"):

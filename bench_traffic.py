@@ -33,6 +33,8 @@ CASES = {
     "decode_paged_c2": (["decode_share_kernel", "decode_merge_kernel"], ["common.h", "decode_core.h", "decode.hip"]),
     "decode_c4": (["decode_share_kernel", "decode_merge_kernel"], ["common.h", "decode_core.h", "decode.hip"]),
     "prefill_c3": (["prefill_pingpong_kernel"], ["common.h", "prefill_core.h", "prefill_pp.h", "prefill.hip"]),
+    "prefill_c3_fp8": (["prefill_fp8_kernel"], ["common.h", "prefill_core.h", "prefill_pp.h", "prefill_fp8.h",
+                                                 "prefill_fp8.hip"]),
     "append_c5": (["kv_append_kernel"], ["append.hip"]),
     "mixed_c5": (["varlen_mixed_kernel", "decode_merge_kernel"],
                  ["common.h", "decode_core.h", "decode.hip", "prefill_core.h", "prefill_pp.h", "prefill.hip"]),

@@ -89,7 +89,9 @@ const char* attn_status_string(attn_status status);
  *   out [total_tokens, num_q_heads, head_dim] bf16 (round to nearest even)
  *   lse [total_tokens, num_q_heads] fp32, or NULL to skip it
  *   max_seqlen: an upper bound on every request's length (sizes the grid)
- * Needs no workspace: nothing but out and lse is written.
+ * Needs no workspace: nothing but out and lse is written. Sizes are checked
+ * first; total_tokens = 0 (or max_seqlen = 0) is then a no-op that returns
+ * ATTN_OK whatever the pointers (empty tensors may pass NULL).
  */
 attn_status attn_prefill_varlen(const void* q, const void* k, const void* v,
                                 const int32_t* cu_seqlens, int32_t causal, float scale, int32_t window,
@@ -97,6 +99,33 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v,
                                 int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                 void* stream);
+
+/*
+ * FP8 varlen prefill ("Attention kernels", section "FlashAttention": the third
+ * version's FP8 variant) on the gfx950 fp8 matrix cores. Inputs are OCP e4m3fn
+ * codes with per-head fp32 scales; the call computes the attention of
+ * attn_prefill_varlen on the decoded values
+ *   Q[t, h, :] = q_scale[h]   * e4m3(q[t, h, :])
+ *   K[t, j, :] = k_scale[j]   * e4m3(k[t, j, :])
+ *   V[t, j, :] = v_scale[j]   * e4m3(v[t, j, :])
+ * with the exponentials P rounded to e4m3 (round to nearest even) for the P V
+ * product; tiles that mask some keys of a row carry P as two e4m3 parts (hi and
+ * the rounding remainder). Row sums and the LSE use the unrounded exponentials.
+ * Results agree with the exact attention of the decoded inputs to within the
+ * fp8 tolerance of the tests (max-abs 3e-2 on out; the LSE to 1e-3).
+ *   q [total_tokens, num_q_heads, 128], k, v [total_tokens, num_kv_heads, 128] uint8 codes;
+ *   every code must be finite (not 0x7F / 0xFF)
+ *   q_scale [num_q_heads], k_scale, v_scale [num_kv_heads] fp32 (device), finite and >= 0
+ *   other arguments and the outputs as for attn_prefill_varlen (window: sliding window, 0 = none)
+ * head_dim other than 128 returns ATTN_ERR_UNSUPPORTED. Needs no workspace;
+ * total_tokens = 0 is a no-op as for attn_prefill_varlen.
+ */
+attn_status attn_prefill_varlen_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                                    const float* k_scale, const float* v_scale, const int32_t* cu_seqlens,
+                                    int32_t causal, float scale, int32_t window, void* out, float* lse,
+                                    int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    void* stream);
 
 /*
  * Number of partitions (partition workgroups) a paged decode call will use

@@ -22,7 +22,7 @@ Modules:
   formats    -- exact decoders: bf16 bit patterns and OCP fp8 e4m3fn codes.
   attention  -- the plain definition (materialised S, max-subtracted softmax,
                 PV, natural-log LSE), naive token-by-token page gather, and the
-                paged decode / mixed varlen entry points built on them.
+                paged decode / mixed varlen / fp8 prefill entry points built on them.
   algorithms -- the pages' tiled algorithms written step by step (online
                 softmax over K blocks, split-KV + LSE merge), used only to pin
                 the pages' claim that they reach the plain definition exactly.
@@ -39,6 +39,7 @@ from .cache import kv_append_paged, quantize_e4m3fn
 from .attention import (
     attend,
     prefill_varlen,
+    prefill_varlen_fp8,
     gather_paged,
     decode_paged,
     varlen_paged,
@@ -54,6 +55,7 @@ __all__ = [
     "E4M3FN_MAX",
     "attend",
     "prefill_varlen",
+    "prefill_varlen_fp8",
     "gather_paged",
     "decode_paged",
     "varlen_paged",

@@ -103,6 +103,22 @@ def prefill_varlen(q, k, v, cu_seqlens, causal, scale, units=None, window=0):
     return out, lse
 
 
+def prefill_varlen_fp8(q_codes, k_codes, v_codes, q_scale, k_scale, v_scale, cu_seqlens, causal, scale,
+                       units=None, window=0):
+    """FP8 varlen prefill ("Attention kernels", section "FlashAttention", the third version's FP8
+    variant): the exact attention of the decoded inputs.
+
+    q_codes [T, Hq, D], k_codes / v_codes [T, Hkv, D] uint8 OCP e4m3fn codes; q_scale [Hq],
+    k_scale / v_scale [Hkv]. Each input is its decoded code times its head's scale, in fp64; the
+    attention itself is ``prefill_varlen`` (materialised S, softmax, P V). Rounding P to fp8 on
+    the way into the P V product is the kernel's approximation of this result, not part of it.
+    """
+    q = decode_e4m3fn(q_codes) * np.asarray(q_scale, dtype=np.float64)[None, :, None]
+    k = decode_e4m3fn(k_codes) * np.asarray(k_scale, dtype=np.float64)[None, :, None]
+    v = decode_e4m3fn(v_codes) * np.asarray(v_scale, dtype=np.float64)[None, :, None]
+    return prefill_varlen(q, k, v, cu_seqlens, causal, scale, units=units, window=window)
+
+
 def gather_paged(k_cache, v_cache, table_row, length, kv_head):
     """Naive page gather for one request and one KV head.
 

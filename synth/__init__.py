@@ -29,7 +29,9 @@ generator); the same seed on different devices gives different numbers.
 from .cases import (
     PrefillCase,
     PagedCase,
+    Fp8PrefillCase,
     make_prefill,
+    make_prefill_fp8,
     make_paged,
     AppendCase,
     make_append,
@@ -40,6 +42,8 @@ from .cases import (
 __all__ = [
     "PrefillCase",
     "PagedCase",
+    "Fp8PrefillCase",
+    "make_prefill_fp8",
     "AppendCase",
     "make_append",
     "make_prefill",

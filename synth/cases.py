@@ -95,6 +95,46 @@ def make_prefill(seed, seqlens, num_q_heads, num_kv_heads, head_dim, causal=True
                        num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim)
 
 
+@dataclass
+class Fp8PrefillCase:
+    """Varlen self-attention over contiguous e4m3fn-coded Q/K/V with per-head fp32 scales."""
+    q: torch.Tensor            # uint8 codes [T, Hq, D]
+    k: torch.Tensor            # uint8 codes [T, Hkv, D]
+    v: torch.Tensor            # uint8 codes [T, Hkv, D]
+    q_scale: torch.Tensor      # fp32 [Hq]
+    k_scale: torch.Tensor      # fp32 [Hkv]
+    v_scale: torch.Tensor      # fp32 [Hkv]
+    cu_seqlens: torch.Tensor   # int32 [B + 1]
+    seqlens: list
+    causal: bool
+    scale: float
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+
+
+def _fp8_codes(x):
+    """fp32 [T, H, D] -> (per-head scale amax_h / 448, e4m3fn codes of x / scale via torch's cast)."""
+    amax = x.abs().amax(dim=(0, 2))
+    head_scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    y = (x / head_scale.view(1, -1, 1)).clamp(-448.0, 448.0)
+    return head_scale.to(torch.float32), y.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def make_prefill_fp8(seed, seqlens, num_q_heads, num_kv_heads, head_dim, causal=True, scale=None, device="cpu"):
+    """FP8 varlen prefill case: Q, then K, then V drawn N(0, 1) in fp32 and cast to e4m3fn codes
+    with per-head scales amax / 448 (the same recipe as the fp8 KV cache)."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    total = int(sum(seqlens))
+    draws = [torch.randn((total, h, head_dim), generator=gen, device=device, dtype=torch.float32)
+             for h in (num_q_heads, num_kv_heads, num_kv_heads)]
+    (qs, qc), (ks, kc), (vs, vc) = (_fp8_codes(x) for x in draws)
+    return Fp8PrefillCase(q=qc, k=kc, v=vc, q_scale=qs, k_scale=ks, v_scale=vs, cu_seqlens=_cu(seqlens, device),
+                          seqlens=[int(x) for x in seqlens], causal=causal,
+                          scale=scale if scale is not None else 1.0 / math.sqrt(head_dim),
+                          num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim)
+
+
 def _kv_draws(gen, kv_lens, num_kv_heads, head_dim, device, chunk_tokens):
     """Yield (request, first_token, values [n, Hkv, D] float32) in a fixed call order,
     so that a second pass from the same generator state repeats the same numbers."""

@@ -14,7 +14,7 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails va
 def declared_functions():
     text = open(_lib.HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -55,6 +55,31 @@ def test_prefill_validation(kw, code):
 
 def test_prefill_empty_batch_is_a_noop():
     assert _prefill(total=0, maxlen=0) == 0
+
+
+def _prefill_fp8(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, qs=FAKE, ks=FAKE, vs=FAKE, cu=FAKE, causal=1, scale=0.1, window=0, out=FAKE,
+                lse=None, nseq=1, total=16, maxlen=16, hq=4, hkv=1, d=128)
+    args.update(kw)
+    return _lib.load().attn_prefill_varlen_fp8(args["q"], args["k"], args["v"], args["qs"], args["ks"], args["vs"],
+                                               args["cu"], args["causal"], args["scale"], args["window"],
+                                               args["out"], args["lse"], args["nseq"], args["total"],
+                                               args["maxlen"], args["hq"], args["hkv"], args["d"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(qs=None), 1), (dict(ks=None), 1),
+    (dict(vs=None), 1), (dict(cu=None), 1), (dict(out=None), 1),
+    (dict(nseq=0), 2), (dict(hq=6, hkv=4), 2), (dict(total=-1), 2), (dict(maxlen=17), 2), (dict(causal=2), 2),
+    (dict(scale=float("inf")), 2), (dict(window=-1), 2),
+    (dict(d=256), 3), (dict(d=64), 3),
+])
+def test_prefill_fp8_validation(kw, code):
+    assert _prefill_fp8(**kw) == code
+
+
+def test_prefill_fp8_empty_batch_is_a_noop():
+    assert _prefill_fp8(total=0, maxlen=0) == 0
 
 
 def _decode(**kw):
