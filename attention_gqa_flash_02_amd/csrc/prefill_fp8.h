@@ -59,9 +59,11 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
 }
 // Four floats -> four e4m3fn codes in one dword (round to nearest even; the values here are in
-// [0, 256], inside the finite range).
+// [0, 256], inside the finite range). The first conversion writes the low half of its third
+// operand and keeps the high half, which the second overwrites, so any starting value will do
+// (a's bits: no register has to be zeroed first).
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 // The two e4m3fn codes in the low (HI = false) or high half of w, decoded to floats.
@@ -141,7 +143,7 @@ __device__ __forceinline__ void prefill_fp8_body(const PrefillFp8Params& p, unsi
   const int lower = win > 0 ? qrow_i - win + 1 : INT_MIN;
   const int wave_mask_from = p.causal ? max(0, tw + 1) : Lk;
 
-  // ---- tile loads, all issued by group B: its wave w (0-3) fills 1 KB blocks LPW*w .. of each
+  // ---- tile loads, all issued by group A: its wave w (0-3) fills 1 KB blocks LPW*w .. of each
   // K and V tile; lane l of a block writes slot l & 7 of row 8 * block + l / 8, i.e. it loads
   // global chunk slot ^ swz(row) of that row
   const long long row_bytes = (long long)p.Hkv * D;
@@ -207,7 +209,7 @@ __device__ __forceinline__ void prefill_fp8_body(const PrefillFp8Params& p, unsi
     for (int i = tid; i < S::LDS_BYTES / 16; i += 512) z[i] = u32x4{0, 0, 0, 0};
   }
   __syncthreads();
-  if (gp == 1 && N > 0) {
+  if (gp == 0 && N > 0) {
     const u32x4 r0 = tile_rsrc(kbase, n_first, true);
 #pragma unroll
     for (int it = 0; it < LPW; ++it) load_block(r0, koff[it], kbuf0 + 1024 * (LPW * lw + it));
@@ -312,8 +314,9 @@ __device__ __forceinline__ void prefill_fp8_body(const PrefillFp8Params& p, unsi
     psplit = split;
   };
   // Group A runs slots 2m (matrix) and 2m+1 (softmax) in iteration m; group B, one slot later,
-  // runs slots 2m+1 (matrix) and 2m+2 (softmax), issuing the tile loads of every even slot 2j
-  // (K j+1, V j) at its start and waiting for them at the end of slot 2j+1.
+  // runs slots 2m+1 (matrix) and 2m+2 (softmax). Group A issues the tile loads of slot 2m (K m+1,
+  // V m) at its start and waits for them at the end of slot 2m+1: its matrix slot has room to
+  // spare, while the softmax slot beside it sets the pace.
   auto issue_loads = [&](int jt) {
     const u32x4 rk = tile_rsrc(kbase, n_first + jt + 1, jt + 1 < N);
     const u32x4 rv = tile_rsrc(vbase, n_first + jt, jt < N);
@@ -327,23 +330,22 @@ __device__ __forceinline__ void prefill_fp8_body(const PrefillFp8Params& p, unsi
   if (gp == 0) {
     for (int m = 0; m <= N; ++m) {
       __builtin_amdgcn_s_setprio(1);
+      if (m < N) issue_loads(m);
       matrix_slot(m);
       __builtin_amdgcn_s_setprio(0);
       __syncthreads();
       if (m < N) softmax_work(m);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
     __syncthreads();
   } else {
-    issue_loads(0);
     __syncthreads();
     for (int m = 0; m <= N; ++m) {
       __builtin_amdgcn_s_setprio(1);
       matrix_slot(m);
       __builtin_amdgcn_s_setprio(0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (m + 1 <= N) issue_loads(m + 1);
       if (m < N) softmax_work(m);
       __syncthreads();
     }

@@ -14,7 +14,7 @@ roofline, checks sampled
 outputs against the fp64 oracle, and times the oracle itself on the host cores
 (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c2|c3|c3fp8|c4|c5|append]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c1|c2|c3|c3fp8|c4|c5|append]
                        [--no-cpu-baseline] [--quick]
 Prints one JSON line.
 """
@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--splits", type=int, default=0, help="decode partitions (0 = library choice)")
-    ap.add_argument("--only", choices=["c2", "c3", "c3fp8", "c4", "c5", "append"], default=None,
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c3fp8", "c4", "c5", "append"], default=None,
                     help="time one workload only (for profiling); the JSON line still names c2's metric")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the parity samples")
@@ -110,12 +110,12 @@ def to_device(case, dev):
     return case
 
 
-def decode_section(lib, case, splits, steps, warmup, label):
+def decode_section(lib, case, splits, steps, warmup, label, rotate=True):
     import torch
     from attention_gqa_flash_02_amd import workmodel
     kv_bytes = workmodel.kv_bytes(case.kv_lens, case.num_kv_heads, case.head_dim,
                                   2 if case.kv_format == "bf16" else 1)
-    copies = max(2, math.ceil(3 * 256e6 / kv_bytes) + 1)
+    copies = max(2, math.ceil(3 * 256e6 / kv_bytes) + 1) if rotate else 1
     caches = [(case.k_cache, case.v_cache)] + [(case.k_cache.clone(), case.v_cache.clone())
                                                for _ in range(copies - 1)]
     b, hq, d = case.q.shape
@@ -362,6 +362,18 @@ def main():
         extra["multi_token_decode"] = multi_token_section(lib, c2, a.steps, a.warmup)
         del c2
         torch.cuda.empty_cache()
+
+    if run("c1"):
+        # the tiny sanity case: latency only (a few microseconds of work, far from any roofline)
+        p1 = synth.config_case("c1_prefill", device=dev)
+        pre1 = prefill_section(lib, p1, a.steps, a.warmup)
+        d1 = synth.config_case("c1_decode", device=dev)
+        dec1 = decode_section(lib, d1, 0, a.steps, a.warmup, "decode c1", rotate=False)
+        extra["c1_latency"] = {
+            "workload": "tiny GQA sanity: causal prefill of 256 tokens (4/1 heads, D 128), then one decode token "
+                        "over 257 cached tokens in 16-token pages",
+            "prefill_us": pre1["kernel_ms_mean"] * 1e3, "decode_us": dec1["kernel_ms_mean"] * 1e3}
+        del p1, d1, pre1, dec1
 
     if run("c3"):
         c3 = synth.config_case("c3", device=dev)
