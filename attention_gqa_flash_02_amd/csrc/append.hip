@@ -8,11 +8,12 @@
 // stores e4m3fn(x / scale[h]): the quotient in correctly rounded fp32, clamped to +-448, converted
 // with round-to-nearest-even.
 //
-// Work layout: a workgroup takes 32 consecutive new-token rows of one kv head. The rows' requests
-// are found with two rounds of loads (a coarse sample of cu_seqlens_new, then the window that
-// holds the first row) and a search in LDS. K rows are copied 16 bytes per thread; V rows are
-// staged in LDS with coalesced loads and written column-wise, consecutive lanes taking
-// consecutive tokens so that each d row of a page is written as one contiguous run.
+// Work layout: a workgroup takes 32 consecutive new-token rows of one kv head. Their K and V rows
+// are loaded into registers first, while the rows' requests are found: a coarse sample of
+// cu_seqlens_new, then (for more than 255 requests) the window that holds the first row, and a
+// search in LDS. K rows are written 16 bytes per thread; V rows are staged in LDS and written
+// column-wise, consecutive lanes taking consecutive tokens so that each d row of a page is
+// written as one contiguous run.
 #include "launch.h"
 
 namespace attn {
@@ -50,6 +51,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 template <int D, bool FP8>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   constexpr int ELT = FP8 ? 1 : 2;
+  constexpr int CPR = D / 8;                   // 16-byte chunks of a bf16 row
+  constexpr int OCH = D * ELT / 16;            // 16-byte output chunks of a cache row
+  constexpr int IPO = 16 / ELT / 8;            // 16-byte input chunks per output chunk (2 for fp8)
+  constexpr int KPT = kAppendRows * OCH / 256; // K output chunks per thread
+  constexpr int VPT = kAppendRows * CPR / 256; // V input chunks per thread
+  static_assert(kAppendRows * OCH % 256 == 0 && kAppendRows * CPR % 256 == 0, "whole chunks per thread");
   __shared__ int s_cu[257];
   __shared__ long long s_kdst[kAppendRows];   // byte offset of each row's K slot
   __shared__ long long s_vdst[kAppendRows];   // element offset of each row's V column (d = 0)
@@ -60,62 +67,86 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   const int nrows = min(kAppendRows, p.total_new - row0);
   const int B = p.num_seqs;
 
-  // ---- requests of the 32 rows: coarse sample, then the window holding the first row
+  // ---- the new K and V rows go into registers first: these loads do not depend on where the
+  // rows land, so they are in flight while the requests and cache slots are looked up
+  u32x4 kin[KPT][IPO], vin[VPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int idx = tid + 256 * i, r = idx / OCH, ch = idx % OCH;
+    const bf16* src = p.k_new + ((size_t)(row0 + r) * p.Hkv + h) * D + IPO * 8 * ch;
+#pragma unroll
+    for (int u = 0; u < IPO; ++u)
+      kin[i][u] = r < nrows ? *reinterpret_cast<const u32x4*>(src + 8 * u) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = tid + 256 * i, r = idx / CPR, ch = idx % CPR;
+    const bf16* src = p.v_new + ((size_t)(row0 + r) * p.Hkv + h) * D + 8 * ch;
+    vin[i] = r < nrows ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+  }
+
+  // ---- requests of the 32 rows: coarse sample, then the window holding the first row (one round
+  // when the whole cu_seqlens_new fits the sample)
   const int step = (B + 256) / 256;            // ceil((B + 1) / 256) requests per sample
   s_cu[tid] = p.cu_seqlens_new[min(tid * step, B)];
+  if (tid == 0) s_cu[256] = p.cu_seqlens_new[B];
   __syncthreads();
-  int lo = 0, hi = 255;                        // largest sample t with cu[t * step] <= row0
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (mid * step <= B && s_cu[mid] <= row0) lo = mid; else hi = mid - 1;
+  int base = 0;
+  if (step > 1) {
+    int lo = 0, hi = 255;                      // largest sample t with cu[t * step] <= row0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (mid * step <= B && s_cu[mid] <= row0) lo = mid; else hi = mid - 1;
+    }
+    base = lo * step;
+    __syncthreads();
+    s_cu[tid] = p.cu_seqlens_new[min(base + tid, B)];
+    if (tid == 0) s_cu[256] = p.cu_seqlens_new[min(base + 256, B)];
+    __syncthreads();
   }
-  const int base = lo * step;
-  __syncthreads();
-  s_cu[tid] = p.cu_seqlens_new[min(base + tid, B)];
-  if (tid == 0) s_cu[256] = p.cu_seqlens_new[min(base + 256, B)];
-  __syncthreads();
   if (tid < nrows) {
     const int row = row0 + tid;
-    int b;
+    int b, c0, c1;
     if (row < s_cu[256] || base + 256 >= B) {  // inside the window: search it in LDS
-      int l2 = 0, h2 = min(256, B - 1 - base);
+      int l2 = 0, h2 = min(256, B - 1 - base);   // l2 <= 255 here, so s_cu[l2 + 1] exists
       while (l2 < h2) {
         const int mid = (l2 + h2 + 1) >> 1;
         if (s_cu[mid] <= row) l2 = mid; else h2 = mid - 1;
       }
       b = base + l2;
+      c0 = s_cu[l2];
+      c1 = s_cu[l2 + 1];
     } else {
       b = request_of_row_global(p.cu_seqlens_new, B, row);
+      c0 = p.cu_seqlens_new[b];
+      c1 = p.cu_seqlens_new[b + 1];
     }
-    const int c0 = p.cu_seqlens_new[b], c1 = p.cu_seqlens_new[b + 1];
     const int pos = p.seq_lens_k[b] - (c1 - c0) + (row - c0);
     const int blk = p.block_table[(size_t)b * p.max_blocks + pos / p.bs];
     const int slot = pos % p.bs;
     s_kdst[tid] = (((long long)blk * p.Hkv + h) * p.bs + slot) * D * ELT;
     s_vdst[tid] = ((long long)blk * p.Hkv + h) * D * p.bs + slot;
   }
-  // ---- V rows into LDS (16-byte loads)
-  constexpr int CPR = D / 8;                   // 16-byte chunks of a bf16 row
-  for (int idx = tid; idx < nrows * CPR; idx += 256) {
-    const int r = idx / CPR, ch = idx % CPR;
-    const bf16* src = p.v_new + ((size_t)(row0 + r) * p.Hkv + h) * D + 8 * ch;
-    *reinterpret_cast<u32x4*>(&s_v[r][8 * ch]) = *reinterpret_cast<const u32x4*>(src);
+  // ---- V rows into LDS
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = tid + 256 * i, r = idx / CPR, ch = idx % CPR;
+    *reinterpret_cast<u32x4*>(&s_v[r][8 * ch]) = vin[i];
   }
   __syncthreads();
 
-  // ---- K rows: 16 output bytes per thread
+  // ---- K rows: 16 output bytes per thread per chunk
   const float ks = FP8 ? p.k_scale[h] : 1.f;
   char* kc = reinterpret_cast<char*>(p.k_cache);
-  constexpr int OCH = D * ELT / 16;            // 16-byte output chunks per row
-  for (int idx = tid; idx < nrows * OCH; idx += 256) {
-    const int r = idx / OCH, ch = idx % OCH;
-    const bf16* src = p.k_new + ((size_t)(row0 + r) * p.Hkv + h) * D;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int idx = tid + 256 * i, r = idx / OCH, ch = idx % OCH;
+    if (r >= nrows) continue;
     char* dst = kc + s_kdst[r] + 16 * ch;
     if constexpr (!FP8) {
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src + 8 * ch);
+      *reinterpret_cast<u32x4*>(dst) = kin[i][0];
     } else {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(src + 16 * ch);
-      const u32x4 c = *reinterpret_cast<const u32x4*>(src + 16 * ch + 8);
+      const u32x4 a = kin[i][0], c = kin[i][IPO - 1];
       u32x4 o;
       o[0] = quant4(bf16_lo(a[0]), bf16_hi(a[0]), bf16_lo(a[1]), bf16_hi(a[1]), ks);
       o[1] = quant4(bf16_lo(a[2]), bf16_hi(a[2]), bf16_lo(a[3]), bf16_hi(a[3]), ks);
