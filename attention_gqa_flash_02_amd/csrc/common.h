@@ -102,10 +102,15 @@ __device__ __forceinline__ float sum_over_quads(float x) {
   return x;
 }
 
-// Non-temporal-free plain global loads of 16 / 8 / 4 bytes.
+// Plain global loads of 16 / 8 / 4 bytes.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ uint32_t ld4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
+// Nontemporal loads (the nt bit: the lines are filled evict-first). For data read once, whole
+// lines at a time, a stream of these reaches about 7.0 TB/s on MI355X against about 6.3 TB/s for
+// plain loads; a line whose other half is read by a later load may have to be fetched twice.
+__device__ __forceinline__ u32x4 ld16nt(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+__device__ __forceinline__ u32x2 ld8nt(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)); }
 
 template <typename T, typename S>
 __device__ __forceinline__ T bitcast(S s) {

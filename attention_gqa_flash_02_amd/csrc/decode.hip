@@ -3,10 +3,10 @@
 
 namespace attn {
 
-template <int D, int KVT, int NU>
+template <int D, int KVT, int NU, bool LONGV>
 __global__ __launch_bounds__(256) void decode_share_kernel(PagedParams p, int combine_floats) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  decode_share<D, KVT, NU>(p, reinterpret_cast<float*>(smem_raw), combine_floats, blockIdx.x);
+  decode_share<D, KVT, NU, LONGV>(p, reinterpret_cast<float*>(smem_raw), combine_floats, blockIdx.x);
 }
 
 template <int D, int CH>
@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(PagedParams p) {
   merge_row<D, CH>(p, blockIdx.z, blockIdx.y, blockIdx.x, reinterpret_cast<float*>(smem_raw));
 }
 
-template <int D, int KVT, int NU>
+template <int D, int KVT, int NU, bool LONGV>
 static hipError_t launch_decode_t(const PagedParams& p, int rows_max, hipStream_t stream) {
   // partition kernel LDS: 128 floats of statistics, four waves' O rows, then the chunk prefix
   // sums and 4 scratch ints
@@ -24,12 +24,12 @@ static hipError_t launch_decode_t(const PagedParams& p, int rows_max, hipStream_
   // the dynamic-LDS limit of each kernel is raised to the largest size launched so far
   static size_t lds_set = 0;
   if (lds > lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_share_kernel<D, KVT, NU>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_share_kernel<D, KVT, NU, LONGV>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     lds_set = lds;
   }
-  hipLaunchKernelGGL((decode_share_kernel<D, KVT, NU>), dim3(p.num_wg), dim3(256), lds, stream, p, combine_floats);
+  hipLaunchKernelGGL((decode_share_kernel<D, KVT, NU, LONGV>), dim3(p.num_wg), dim3(256), lds, stream, p, combine_floats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_merge(p, D, NU, rows_max, stream);
@@ -58,11 +58,17 @@ hipError_t launch_decode_merge(const PagedParams& p, int head_dim, int nu, int r
   return hipErrorInvalidValue;
 }
 
+template <int D, int KVT, int NU>
+static hipError_t launch_decode_bs(const PagedParams& p, int rows_max, hipStream_t stream) {
+  return p.bs > 32 ? launch_decode_t<D, KVT, NU, true>(p, rows_max, stream)
+                   : launch_decode_t<D, KVT, NU, false>(p, rows_max, stream);
+}
+
 hipError_t launch_decode(const PagedParams& p, int head_dim, int kv_type, int rows_max, hipStream_t stream) {
-  if (head_dim == 128 && kv_type == KV_BF16) return launch_decode_t<128, KV_BF16, 4>(p, rows_max, stream);
-  if (head_dim == 256 && kv_type == KV_BF16) return launch_decode_t<256, KV_BF16, 2>(p, rows_max, stream);
-  if (head_dim == 128 && kv_type == KV_FP8) return launch_decode_t<128, KV_FP8, 4>(p, rows_max, stream);
-  if (head_dim == 256 && kv_type == KV_FP8) return launch_decode_t<256, KV_FP8, 2>(p, rows_max, stream);
+  if (head_dim == 128 && kv_type == KV_BF16) return launch_decode_bs<128, KV_BF16, 4>(p, rows_max, stream);
+  if (head_dim == 256 && kv_type == KV_BF16) return launch_decode_bs<256, KV_BF16, 2>(p, rows_max, stream);
+  if (head_dim == 128 && kv_type == KV_FP8) return launch_decode_bs<128, KV_FP8, 4>(p, rows_max, stream);
+  if (head_dim == 256 && kv_type == KV_FP8) return launch_decode_bs<256, KV_FP8, 2>(p, rows_max, stream);
   return hipErrorInvalidValue;
 }
 
@@ -74,14 +80,19 @@ int decode_chunk_tokens(int head_dim, int kv_type) {
 template <int D, int KVT, int NU>
 static int wgs_per_cu_t() {
   // Resident partition workgroups per compute unit (the register-limited occupancy of the
-  // variant), queried once; a failed query leaves no pending error and counts as 1.
+  // variant; the smaller of its two V-load forms), queried once; a failed query leaves no
+  // pending error and counts as 1.
   static int cached = 0;
   if (cached > 0) return cached;
-  int n = 0;
-  const void* fn = reinterpret_cast<const void*>(&decode_share_kernel<D, KVT, NU>);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, 16 * 1024) != hipSuccess || n < 1) {
-    (void)hipGetLastError();
-    n = 1;
+  int n = INT_MAX;
+  for (const void* fn : {reinterpret_cast<const void*>(&decode_share_kernel<D, KVT, NU, false>),
+                         reinterpret_cast<const void*>(&decode_share_kernel<D, KVT, NU, true>)}) {
+    int m = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, fn, 256, 16 * 1024) != hipSuccess || m < 1) {
+      (void)hipGetLastError();
+      m = 1;
+    }
+    n = std::min(n, m);
   }
   cached = n;
   return n;

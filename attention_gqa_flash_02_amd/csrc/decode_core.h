@@ -108,8 +108,9 @@ struct DecodeShape {
 // One piece of a (request, kv head) unit: chunks [c0, c1) of the unit; the waves start at chunk
 // c0 + first[w] and step by 4 chunks. Rows of a request on this path: r -> (new token r / g,
 // query head kvh*g + r % g). slot < 0: the piece is the whole unit and is written to out/lse;
-// else it is written to partial slot `slot` of the workspace.
-template <int D, int KVT, int NU>
+// else it is written to partial slot `slot` of the workspace. LONGV: V page rows are longer than
+// one 32-token half (block size > 32), which decides how the V loads are issued.
+template <int D, int KVT, int NU, bool LONGV>
 __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kvh, int c0, int c1, int wave_first,
                                              int share, int slot, float* lds) {
   constexpr int CH = DecodeShape<NU>::CH;
@@ -225,17 +226,32 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
       }
     }
     // V: 8 consecutive tokens of one d row per lane and d block (16 bytes bf16, 8 bytes fp8).
+    // The V stream is read once, so its loads are nontemporal where every line they touch is
+    // read whole by loads issued back to back: with block size <= 32 a half covers whole page
+    // rows; with longer rows the two halves of a chunk share each line and are issued in pairs.
+    // With one half per chunk the rest of each line belongs to another chunk: plain loads.
     vword vraw[NH][NB];
+    const char* vrun[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const int vslot = (T0 + 32 * h) % p.bs + vq8;
-      const char* vrun = vc + (size_t)vphys[h] * block_stride + ((size_t)j * p.bs + vslot) * ELT;
+      vrun[h] = vc + (size_t)vphys[h] * block_stride + ((size_t)j * p.bs + vslot) * ELT;
+    }
+    auto vload = [&](int h, int n, bool nt) {
+      const char* vrow = vrun[h] + (size_t)16 * n * p.bs * ELT;
+      if constexpr (KVT == KV_BF16) vraw[h][n] = nt ? ld16nt(vrow) : ld16(vrow);
+      else vraw[h][n] = nt ? ld8nt(vrow) : ld8(vrow);
+    };
+    if constexpr (!LONGV) {
 #pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const char* vrow = vrun + (size_t)16 * n * p.bs * ELT;
-        if constexpr (KVT == KV_BF16) vraw[h][n] = ld16(vrow);
-        else vraw[h][n] = ld8(vrow);
-      }
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) vload(h, n, true);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) vload(h, n, NH == 2);
     }
     // ---------------- block-table entries of this wave's next chunk
     const int Tn = T0 + 4 * CH;
@@ -431,7 +447,7 @@ __device__ __forceinline__ void block_prefix(int B, Count count, int* sp, int* w
 
 // The partition kernel's body: share g of the batch's chunks walks the (request, kv head)
 // pieces it covers. lds: the combine buffer of decode_piece, then sp[B + 1] and 4 scratch ints.
-template <int D, int KVT, int NU>
+template <int D, int KVT, int NU, bool LONGV>
 __device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, int combine_floats, int g) {
   constexpr int CH = DecodeShape<NU>::CH;
   int* sp = reinterpret_cast<int*>(lds + combine_floats);
@@ -463,7 +479,7 @@ __device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, i
     // chunks are dealt to the waves round-robin over the whole share
     const int wave_first = (int)((wave - (pos - r0) % 4 + 4) % 4);
     const int slot = (c0 == 0 && c1 == nb) ? -1 : (first ? 0 : 1);
-    decode_piece<D, KVT, NU>(p, b, kvh, c0, c1, wave_first, g, slot, lds);
+    decode_piece<D, KVT, NU, LONGV>(p, b, kvh, c0, c1, wave_first, g, slot, lds);
     pos += c1 - c0;
     first = false;
     if (c1 == nb && kvh == p.Hkv - 1) ++b;

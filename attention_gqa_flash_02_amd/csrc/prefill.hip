@@ -37,14 +37,14 @@ __device__ __forceinline__ int prefill_qtiles(const PrefillParams& p, int b, int
 // Mixed varlen batch over a paged cache in one launch: workgroups [0, n_dec) are the decode
 // path's shares (memory-bound; dispatched first so that they run beside the prefill tiles), the
 // rest are prefill q-tiles (compute-bound), heaviest tile of each request first.
-template <int D, int BN, int KVT, int NU>
+template <int D, int BN, int KVT, int NU, bool LONGV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D>(), prefill_waves_per_eu<D>())))
 void varlen_mixed_kernel(PrefillParams pp, PagedParams dp, int n_dec,
                                                            int combine_floats) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* lds = reinterpret_cast<float*>(smem_raw);
   if ((int)blockIdx.x < n_dec) {
-    decode_share<D, KVT, NU>(dp, lds, combine_floats, blockIdx.x);
+    decode_share<D, KVT, NU, LONGV>(dp, lds, combine_floats, blockIdx.x);
     return;
   }
   using Loader = PagedLoader<D, BN, KVT == KV_FP8>;
@@ -110,7 +110,7 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, 
   return hipErrorInvalidValue;
 }
 
-template <int D, int BN, int KVT, int NU>
+template <int D, int BN, int KVT, int NU, bool LONGV>
 static hipError_t launch_mixed_t(const PrefillParams& pp, const PagedParams& dp, int total_q, hipStream_t stream) {
   const int tq = 32 * (4 / pp.hpw);
   // upper bound on prefill q-tiles: every request adds at most one partial tile
@@ -122,24 +122,30 @@ static hipError_t launch_mixed_t(const PrefillParams& pp, const PagedParams& dp,
   const size_t lds = std::max((size_t)PrefillShape<D, BN>::LDS_BYTES, (size_t)combine_floats * sizeof(float)) + ints;
   static size_t lds_set = 0;
   if (lds > lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&varlen_mixed_kernel<D, BN, KVT, NU>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     lds_set = lds;
   }
-  hipLaunchKernelGGL((varlen_mixed_kernel<D, BN, KVT, NU>), dim3((unsigned)(n_pre + n_dec)), dim3(256), lds, stream,
+  hipLaunchKernelGGL((varlen_mixed_kernel<D, BN, KVT, NU, LONGV>), dim3((unsigned)(n_pre + n_dec)), dim3(256), lds, stream,
                      pp, dp, n_dec, combine_floats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_merge(dp, D, NU, 16, stream);
 }
 
+template <int D, int BN, int KVT, int NU>
+static hipError_t launch_mixed_bs(const PrefillParams& pp, const PagedParams& dp, int total_q, hipStream_t stream) {
+  return dp.bs > 32 ? launch_mixed_t<D, BN, KVT, NU, true>(pp, dp, total_q, stream)
+                    : launch_mixed_t<D, BN, KVT, NU, false>(pp, dp, total_q, stream);
+}
+
 hipError_t launch_mixed(const PrefillParams& pp, const PagedParams& dp, int head_dim, int kv_type, int total_q,
                         hipStream_t stream) {
-  if (head_dim == 128 && kv_type == KV_BF16) return launch_mixed_t<128, 64, KV_BF16, 4>(pp, dp, total_q, stream);
-  if (head_dim == 256 && kv_type == KV_BF16) return launch_mixed_t<256, 64, KV_BF16, 2>(pp, dp, total_q, stream);
-  if (head_dim == 128 && kv_type == KV_FP8) return launch_mixed_t<128, 64, KV_FP8, 4>(pp, dp, total_q, stream);
-  if (head_dim == 256 && kv_type == KV_FP8) return launch_mixed_t<256, 64, KV_FP8, 2>(pp, dp, total_q, stream);
+  if (head_dim == 128 && kv_type == KV_BF16) return launch_mixed_bs<128, 64, KV_BF16, 4>(pp, dp, total_q, stream);
+  if (head_dim == 256 && kv_type == KV_BF16) return launch_mixed_bs<256, 64, KV_BF16, 2>(pp, dp, total_q, stream);
+  if (head_dim == 128 && kv_type == KV_FP8) return launch_mixed_bs<128, 64, KV_FP8, 4>(pp, dp, total_q, stream);
+  if (head_dim == 256 && kv_type == KV_FP8) return launch_mixed_bs<256, 64, KV_FP8, 2>(pp, dp, total_q, stream);
   return hipErrorInvalidValue;
 }
 
