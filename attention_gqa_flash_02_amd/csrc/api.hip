@@ -41,7 +41,7 @@ static int gcd_int(int a, int b) {
   return a;
 }
 
-// Upper bound on decode partitions: the merge kernel keeps one weight per partition in LDS.
+// Upper bound on decode partitions (it bounds the workspace: two partial slots per partition).
 constexpr int kMaxSplits = 4096;
 // Upper bound on requests of a paged call: the partition kernel keeps one chunk offset per
 // request in LDS.

@@ -37,7 +37,7 @@ static hipError_t launch_decode_t(const PagedParams& p, int rows_max, hipStream_
 
 template <int D, int CH>
 static hipError_t launch_merge_t(const PagedParams& p, int rows_max, hipStream_t stream) {
-  const size_t merge_lds = ((size_t)p.num_wg + (256 / (D / 4)) * D) * sizeof(float);
+  const size_t merge_lds = (size_t)(256 / (D / 4)) * (D + 2) * sizeof(float);
   static size_t merge_lds_set = 0;
   if (merge_lds > merge_lds_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_merge_kernel<D, CH>),

@@ -489,10 +489,11 @@ __device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, i
 // Merge of the pieces of one (request, kv head, row) that spans several shares, with
 // natural-log LSE weights ("Attention kernels", section "Prefill and decode attention": partial
 // results combined the same way as the online softmax). Also writes out = 0, lse = -inf for
-// rows of a request with no key. Latency-bound, so every phase issues all of its loads at once:
-// (1) the pieces' LSEs into LDS, (2) the weights, (3) thread t sums d-quad t % (D/4) over the
-// pieces t / (D/4) + k * 256/(D/4), eight loads in flight, and the groups are added in LDS in a
-// fixed order. lds: lse/weights[G] then sums[256/(D/4)][D].
+// rows of a request with no key. Latency-bound, so it takes two dependent memory round trips:
+// the chunk offsets, then every piece's LSE and partial output together. Thread t handles d-quad
+// t % (D/4) of the pieces t / (D/4) + k * 256/(D/4) (eight in flight) and folds them into a
+// running (max, sum, output); the thread groups are then combined in LDS in a fixed order.
+// lds: per group its maximum and sum, then its output row.
 template <int D, int CH>
 __device__ __forceinline__ void merge_row(const PagedParams& p, int b, int kvh, int r, float* lds) {
   constexpr int DQ = D / 4;
@@ -501,7 +502,7 @@ __device__ __forceinline__ void merge_row(const PagedParams& p, int b, int kvh, 
   const int qlen = p.cu_seqlens_q ? (p.cu_seqlens_q[b + 1] - q0) : 1;
   const int R = qlen * p.g;
   if (R > 16 || r >= R) return;                        // rows of another path, or no such row
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int i = r / p.g, h = kvh * p.g + r % p.g;
   bf16* orow = p.out + ((size_t)(q0 + i) * p.Hq + h) * D;
   const int nb = p.ws_prefix[b + 1] - p.ws_prefix[b];
@@ -518,55 +519,61 @@ __device__ __forceinline__ void merge_row(const PagedParams& p, int b, int kvh, 
   const int ns = g_hi - g_lo + 1;
   // piece k lives in share g_lo + k: slot 0 (the unit is that share's first unit) except for the
   // first piece when the unit began inside share g_lo's range after another unit. Empty shares
-  // (when there are fewer chunk groups than shares) hold no piece and get weight 0.
+  // (when there are fewer chunk groups than shares) hold no piece and are skipped.
   const int slot_lo = (share_start(g_lo, T, G) == start) ? 0 : 1;
-  auto piece = [&](int k) { return (size_t)(g_lo + k) * 2 + (k == 0 ? slot_lo : 0); };
-  float* w = lds;
-  float* red = lds + G;
-  __shared__ float s_max, s_sum;
-  for (int k = tid; k < ns; k += 256) {
-    const bool has = share_start(g_lo + k, T, G) < share_start(g_lo + k + 1, T, G);
-    w[k] = has ? p.ws_lse[piece(k) * 16 + r] : kNegInf;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    float mx = kNegInf;
-    for (int k = lane; k < ns; k += 64) mx = fmaxf(mx, w[k]);
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-    float sum = 0.f;
-    for (int k = lane; k < ns; k += 64) {
-      const float ls = w[k];
-      const float e = (mx == kNegInf || ls == kNegInf) ? 0.f : fast_exp2((ls - mx) * kLog2e);
-      w[k] = e;
-      sum += e;
-    }
-    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-    if (lane == 0) { s_max = mx; s_sum = sum; }
-  }
-  __syncthreads();
   const int dq = tid % DQ, grp = tid / DQ;
-  const float* src = p.ws_o + (size_t)r * D + 4 * dq;
-  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+  float M = kNegInf, S = 0.f;
+  f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = grp; k0 < ns; k0 += 8 * GROUPS) {
-    f32x4 part[8];
-    float wk[8];
+    float lk[8];
+    f32x4 ok[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int k = k0 + u * GROUPS;
-      wk[u] = (k < ns) ? w[k] : 0.f;
-      part[u] = (wk[u] != 0.f) ? *reinterpret_cast<const f32x4*>(src + piece(k) * 16 * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const int gk = g_lo + k;
+      const bool has = k < ns && share_start(gk, T, G) < share_start(gk + 1, T, G);
+      const size_t piece = (size_t)gk * 2 + (k == 0 ? slot_lo : 0);
+      lk[u] = has ? p.ws_lse[piece * 16 + r] : kNegInf;
+      ok[u] = has ? *reinterpret_cast<const f32x4*>(p.ws_o + (piece * 16 + r) * D + 4 * dq)
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) o += part[u] * wk[u];
+    for (int u = 0; u < 8; ++u) {
+      if (lk[u] == kNegInf) continue;
+      const float m2 = fmaxf(M, lk[u]);
+      const float a = (M == kNegInf) ? 0.f : fast_exp2((M - m2) * kLog2e);
+      const float w = fast_exp2((lk[u] - m2) * kLog2e);
+      S = S * a + w;
+      O = O * a + ok[u] * w;
+      M = m2;
+    }
   }
-  *reinterpret_cast<f32x4*>(red + grp * D + 4 * dq) = o;
+  float* gstat = lds;                                  // [GROUPS][2]: maximum, sum
+  float* gout = lds + 2 * GROUPS;                      // [GROUPS][D]
+  if (dq == 0) {
+    gstat[2 * grp] = M;
+    gstat[2 * grp + 1] = S;
+  }
+  *reinterpret_cast<f32x4*>(gout + grp * D + 4 * dq) = O;
   __syncthreads();
   if (grp == 0) {
-    for (int g2 = 1; g2 < GROUPS; ++g2) o += *reinterpret_cast<const f32x4*>(red + g2 * D + 4 * dq);
-    const float inv = (s_sum > 0.f) ? 1.f / s_sum : 0.f;
-    *reinterpret_cast<bf16x4*>(orow + 4 * dq) = f32x4_to_bf16x4(o * inv);
+    float mt = kNegInf;
+#pragma unroll
+    for (int g2 = 0; g2 < GROUPS; ++g2) mt = fmaxf(mt, gstat[2 * g2]);
+    float st = 0.f;
+    f32x4 ot = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g2 = 0; g2 < GROUPS; ++g2) {
+      const float mg = gstat[2 * g2];
+      if (mg == kNegInf) continue;
+      const float w = fast_exp2((mg - mt) * kLog2e);
+      st += gstat[2 * g2 + 1] * w;
+      ot += *reinterpret_cast<const f32x4*>(gout + g2 * D + 4 * dq) * w;
+    }
+    const float inv = (st > 0.f) ? 1.f / st : 0.f;
+    *reinterpret_cast<bf16x4*>(orow + 4 * dq) = f32x4_to_bf16x4(ot * inv);
     if (p.lse && dq == 0)
-      p.lse[(size_t)(q0 + i) * p.Hq + h] = (s_sum > 0.f) ? s_max + kLn2 * fast_log2(s_sum) : kNegInf;
+      p.lse[(size_t)(q0 + i) * p.Hq + h] = (st > 0.f) ? mt + kLn2 * fast_log2(st) : kNegInf;
   }
 }
 

@@ -85,6 +85,23 @@ def test_decode_c4_shrunk(gpu, splits):
     compare(out, lse, ref_o, ref_l, label=f"c4/32 splits={splits}")
 
 
+def test_decode_workspace_reuse(gpu):
+    """One workspace, filled with arbitrary bytes first, serves calls of different shapes and split
+    counts in a row; every call matches the oracle (the workspace needs no initialisation)."""
+    gen = torch.Generator().manual_seed(77)
+    cases = [_to(synth.config_case("c2", shrink=4), gpu),
+             _to(synth.make_paged(78, [1, 40, 700, 3000, 0, 129], [1] * 6, 8, 2, 128, 16, lengths_drawn=gen), gpu),
+             _to(synth.config_case("c4", shrink=32), gpu)]
+    ws = torch.randint(0, 256, (1 << 23,), dtype=torch.uint8, generator=gen).to(gpu)
+    for case, splits in [(cases[0], 16), (cases[0], 16), (cases[1], 8), (cases[0], 64), (cases[2], 16),
+                         (cases[2], 64), (cases[1], 3), (cases[0], 0)]:
+        out, lse = lib.attn_decode_paged(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens_k,
+                                         case.scale, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle_paged(case)
+        compare(out, lse, ref_o, ref_l, label=f"workspace reuse B={case.q.shape[0]} splits={splits}")
+
+
 @pytest.mark.parametrize("d,bs", [(256, 16), (128, 32), (128, 16)])
 def test_decode_fp8(gpu, d, bs):
     lens = [1, 15, 16, 17, 300, 1000]
