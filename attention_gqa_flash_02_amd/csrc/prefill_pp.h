@@ -25,10 +25,12 @@
 // Loads past the request's last key read zero (range-checked buffer resource).
 //
 // Schedule, with m = tile index counted from the first tile the workgroup sees:
-//   slot 2m:   A: P V (m-1), S^T (m)        B: softmax (m-1), then issue the loads of K (m+1), V (m)
-//   slot 2m+1: A: softmax (m)               B: P V (m-1), S^T (m), then wait for those loads
-// K (m+1) goes into the buffer of K (m-1), and V (m) into that of V (m-2). Both were last read in
-// slot 2m-1 and both are first read in slot 2m+2. Every wave runs every tile of its workgroup:
+//   slot 2m:   A: P V (m-1), S^T (m)        B: issue batch m+1, then softmax (m-1)
+//   slot 2m+1: A: softmax (m)               B: P V (m-1), S^T (m), then wait for batch m
+// Batch j holds the loads of K (j+1) and V (j). K and V have three LDS buffers each (tile n in
+// buffer n mod 3), so batch j, issued in slot 2j-2, overwrites K (j-2) and V (j-3), both last
+// read in slot 2j-3, and is waited for at the end of slot 2j+1, before its first read in slot
+// 2j+2: a load has four slots of latency. Every wave runs every tile of its workgroup:
 // tiles that a wave's rows do not see are masked. The control flow is therefore uniform, and every
 // slot runs the same straight-line MFMA stream.
 #pragma once
@@ -48,7 +50,8 @@ struct PingPongShape {
   static constexpr int D = 128;
   static constexpr int ROW = 2 * D;                  // bytes per key row in LDS
   static constexpr int TILE = BN * ROW;              // bytes per K or V tile
-  static constexpr int LDS_BYTES = 4 * TILE;         // K0 K1 V0 V1
+  static constexpr int NBUF = 3;                     // LDS buffers per K and V
+  static constexpr int LDS_BYTES = 2 * NBUF * TILE;  // K0 K1 K2 V0 V1 V2
   static constexpr int BLOCKS = TILE / 1024;         // 1 KB load blocks per tile
   static_assert(BLOCKS % 4 == 0, "each of the 4 loading waves fills whole 1 KB blocks");
 };
@@ -131,8 +134,9 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
     koff[it] = (int)(row * row_bytes) + 16 * (slot ^ swz_k(row));
     voff[it] = (int)(row * row_bytes) + 16 * (slot ^ swz_v(row));
   }
+  constexpr int NBUF = S::NBUF;
   unsigned char* const kbuf0 = smem;
-  unsigned char* const vbuf0 = smem + 2 * S::TILE;
+  unsigned char* const vbuf0 = smem + NBUF * S::TILE;
   // Buffer resource of tile n (no bytes when the tile does not exist: its loads then read zero).
   auto tile_rsrc = [&](const char* base, int n, bool exists) -> u32x4 {
     const long long t = (long long)n * BN * row_bytes;
@@ -169,9 +173,15 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int chunk = 4 * db + 2 * (g & 1) + (a >> 1);
-        vaddr[db][r] = rowb * S::ROW + 16 * (chunk ^ swz_v(rowb)) + 8 * (a & 1);
+        vaddr[db][r] = NBUF * S::TILE + rowb * S::ROW + 16 * (chunk ^ swz_v(rowb)) + 8 * (a & 1);
       }
     }
+    // The V addresses include the offset of the first V buffer and are kept opaque, so that a read
+    // of V buffer b only adds b * TILE (an immediate below 64 KB) to them.
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(vaddr[db][r]));
   }
 
   f32x16 acc[NDB];
@@ -222,9 +232,13 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
     const i16x4 v1 = lds_read_tr(vt + vaddr[db][1]);
     return bitcast<bf16x8>(__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto matrix_slot = [&](int m) {
-    const unsigned char* Vt = vbuf0 + ((m - 1) & 1) * S::TILE;
-    const unsigned char* Ks = kbuf0 + (m & 1) * S::TILE;
+  // The buffer indices are compile-time constants (the slot loop is unrolled by NBUF), so the
+  // operand reads address every buffer with an immediate offset.
+  auto matrix_slot = [&](auto kb_c) {
+    constexpr int KB = decltype(kb_c)::value;          // K (m) is in buffer m % NBUF
+    constexpr int VB = (KB + NBUF - 1) % NBUF;         // V (m-1)
+    const unsigned char* Vt = smem + VB * S::TILE;     // + vaddr = V buffer VB
+    const unsigned char* Ks = kbuf0 + KB * S::TILE;
     auto fetch = [&](int i) -> bf16x8 {
       if ((i & 1) == 0) return v_operand(Vt, i >> 1);
       const int k = i >> 1, kk = k / NKB, kb = k % NKB;
@@ -318,38 +332,63 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
   // runs slots 2m+1 (matrix) and 2m+2 (softmax), and it issues the tile loads of every even slot 2j
   // (K j+1 and V j) at its start and waits for them at the end of slot 2j+1. The matrix work runs
   // at a raised wave priority, so that the SIMD's other wave never holds up an MFMA's issue.
-  auto issue_loads = [&](int j) {
+  auto issue_loads = [&](int j, auto jb_c) {
+    constexpr int JB = decltype(jb_c)::value;          // j % NBUF
     const u32x4 rk = tile_rsrc(kbase, n_first + j + 1, j + 1 < N);
     const u32x4 rv = tile_rsrc(vbase, n_first + j, j < N);
-    unsigned char* kdst = kbuf0 + ((j + 1) & 1) * S::TILE + 1024 * LPW * lw;
-    unsigned char* vdst = vbuf0 + (j & 1) * S::TILE + 1024 * LPW * lw;
+    unsigned char* kdst = kbuf0 + ((JB + 1) % NBUF) * S::TILE + 1024 * LPW * lw;
+    unsigned char* vdst = vbuf0 + JB * S::TILE + 1024 * LPW * lw;
 #pragma unroll
     for (int q = 0; q < LPW; ++q) load_block(rk, koff[q], kdst + 1024 * q);
 #pragma unroll
     for (int q = 0; q < LPW; ++q) load_block(rv, voff[q], vdst + 1024 * q);
   };
+  static_assert(NBUF == 3, "the slot loop below is unrolled by 3");
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   if (gp == 0) {
-    for (int m = 0; m <= N; ++m) {
+    auto step = [&](int m, auto kb_c) {
+      if (m > N) return;
       __builtin_amdgcn_s_setprio(1);
-      matrix_slot(m);
+      matrix_slot(kb_c);
       __builtin_amdgcn_s_setprio(0);
       __syncthreads();
       if (m < N) softmax_work(m);
       __syncthreads();
+    };
+    for (int m = 0; m <= N; m += 3) {
+      step(m, I0{});
+      step(m + 1, I1{});
+      step(m + 2, I2{});
     }
     __syncthreads();
   } else {
-    issue_loads(0);
+    // Batch j = the loads of K (j+1) and V (j). Batches 0 and 1 go out in slot 0; batch m+2 goes
+    // out at the start of slot 2m+2 and batch m is waited for at the end of slot 2m+1, so a load
+    // has four slots of latency.
+    static_assert(2 * LPW == 8, "a batch is 8 loads per wave (the vmcnt below)");
+    issue_loads(0, I0{});
+    if (1 <= N) issue_loads(1, I1{});
     __syncthreads();
-    for (int m = 0; m <= N; ++m) {
+    auto step = [&](int m, auto kb_c) {
+      constexpr int KB = decltype(kb_c)::value;
+      if (m > N) return;
       __builtin_amdgcn_s_setprio(1);
-      matrix_slot(m);
+      matrix_slot(kb_c);
       __builtin_amdgcn_s_setprio(0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // wait for batch m only: batch m+1, issued after it, may stay in flight
+      if (m + 1 <= N) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (m + 1 <= N) issue_loads(m + 1);
+      if (m + 2 <= N) issue_loads(m + 2, std::integral_constant<int, (KB + 2) % 3>{});
       if (m < N) softmax_work(m);
       __syncthreads();
+    };
+    for (int m = 0; m <= N; m += 3) {
+      step(m, I0{});
+      step(m + 1, I1{});
+      step(m + 2, I2{});
     }
   }
 
