@@ -245,6 +245,7 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
       !(std::isfinite(scale) && scale >= 0.f) || window < 0)
     return ATTN_ERR_SHAPE;
   if ((long long)total_q * num_q_heads * head_dim > (long long)INT_MAX * 8) return ATTN_ERR_SHAPE;
+  if (num_seqs > mixed_max_seqs(head_dim)) return ATTN_ERR_UNSUPPORTED;
   const int S = attn_decode_num_splits(num_seqs, num_kv_heads, head_dim, kv_dtype, block_size,
                                        max_blocks_per_seq, num_splits);
   const size_t need = attn_varlen_workspace_bytes(num_seqs, num_kv_heads, head_dim, S);

@@ -31,6 +31,8 @@ hipError_t launch_decode_merge(const PagedParams& p, int head_dim, int nu, int r
 
 // Mixed varlen batch over a paged cache: one launch holding the decode path's p.num_wg shares
 // and the prefill q-tiles, then the merge.
+// Largest num_seqs a mixed call of this head_dim supports (its LDS holds per-request offsets).
+int mixed_max_seqs(int head_dim);
 hipError_t launch_mixed(const PrefillParams& pp, const PagedParams& dp, int head_dim, int kv_type, int total_q,
                         hipStream_t stream);
 

@@ -140,6 +140,19 @@ static hipError_t launch_mixed_bs(const PrefillParams& pp, const PagedParams& dp
                     : launch_mixed_t<D, BN, KVT, NU, false>(pp, dp, total_q, stream);
 }
 
+// Largest request count whose mixed-kernel LDS (the larger of the prefill tile buffers and the
+// decode combine buffer, then num_seqs + 5 ints) fits the 160 KB a workgroup may hold.
+template <int D>
+static int mixed_max_seqs_t() {
+  constexpr long long kMaxLds = 160 * 1024;
+  const long long base = std::max((long long)PrefillShape<D, 64>::LDS_BYTES, (long long)(128 + 4 * 16 * D) * 4);
+  return (int)std::min<long long>((kMaxLds - base) / 4 - 5, INT_MAX);
+}
+
+int mixed_max_seqs(int head_dim) {
+  return head_dim == 128 ? mixed_max_seqs_t<128>() : mixed_max_seqs_t<256>();
+}
+
 hipError_t launch_mixed(const PrefillParams& pp, const PagedParams& dp, int head_dim, int kv_type, int total_q,
                         hipStream_t stream) {
   if (head_dim == 128 && kv_type == KV_BF16) return launch_mixed_bs<128, 64, KV_BF16, 4>(pp, dp, total_q, stream);
