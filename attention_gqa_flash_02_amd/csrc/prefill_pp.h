@@ -110,8 +110,6 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qB[kk] = bf16x8{};
   }
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qB[kk]));
   const int lim = p.causal ? min(qrow_i, Lk - 1) : (Lk - 1);
   const int lower = win > 0 ? qrow_i - win + 1 : INT_MIN;
   const int wave_mask_from = p.causal ? max(0, tw + 1) : Lk;
@@ -191,7 +189,10 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   float mc = kNegInf, l = 0.f;
 
-  // LDS starts zeroed (a load past the keys leaves its slots as they were), then K of the first tile
+  // LDS starts zeroed (a load past the keys leaves its slots as they were), then K of the first tile.
+  // The Q loads, issued first, are waited for only here, together with that tile, so the two
+  // latencies overlap. An empty asm then redefines the Q registers, so the tile loop never waits on
+  // the memory counter for them (which would also wait for the tile loads in flight).
   {
     u32x4* z = reinterpret_cast<u32x4*>(smem);
     for (int i = tid; i < S::LDS_BYTES / 16; i += 512) z[i] = u32x4{0, 0, 0, 0};
@@ -203,6 +204,8 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
     for (int it = 0; it < LPW; ++it) load_block(r0, koff[it], kbuf0 + 1024 * (LPW * lw + it));
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qB[kk]));
   __syncthreads();
 
   f32x16 st[NKB];
