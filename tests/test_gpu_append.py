@@ -69,3 +69,35 @@ def test_append_many_requests_and_rounding_ties(gpu):
 def test_append_empty_is_a_noop(gpu):
     case = synth.make_append(3, [4, 9], [0, 0], 2, 128, 16, "bf16")
     _check(case, gpu)
+
+
+def test_append_quotient_edges(gpu):
+    """fp8 quotients x / scale at the edges of the quantiser's reciprocal path: heads whose scale
+    or reciprocal is subnormal (those divide), a scale just below a power of two, inputs below
+    2^-96 (bf16 subnormals, +-0), and inputs placed so that x / scale lands next to e4m3
+    midpoints. Every quotient stays finite (the oracle's encoder takes finite values)."""
+    d, hkv = 128, 4
+    new = [40, 1, 23]
+    scales = [1e-38, 1e38, 0.0123, float(np.nextafter(np.float32(2.0 ** -20), np.float32(0))),   # K heads
+              2.0 ** -126, 3.0e37, 0.3, 1.0]                                                       # V heads
+    case = synth.make_append(91, [3, 0, 17], new, hkv, d, 16, "e4m3fn", scales=scales)
+    g = np.random.default_rng(91)
+    rows = sum(new)
+    vals = oracle.decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float64)
+    for t, sc in ((case.k_new, case.k_scale.numpy()), (case.v_new, case.v_scale.numpy())):
+        x = np.empty((rows, hkv, d), dtype=np.float32)
+        for h in range(hkv):
+            s = np.float64(sc[h])
+            # quotients near every e4m3 midpoint (one bf16 rounding away), random magnitudes, tiny
+            # inputs: bf16 subnormals, values around 2^-96, signed zeros
+            near = (g.choice(mids, rows * d // 2) * s * g.choice([-1, 1], rows * d // 2))
+            wide = g.standard_normal(rows * d // 4) * 10.0 ** g.uniform(-30, 0, rows * d // 4)
+            tiny = np.concatenate([g.uniform(-1, 1, rows * d // 8) * 2.0 ** -100,
+                                   g.uniform(-1, 1, rows * d // 16) * 1e-39, [0.0, -0.0]])
+            col = np.concatenate([near, wide, tiny])
+            col = np.resize(col, rows * d)
+            col = np.clip(col, -3.0, 3.0)                     # finite quotients for the 1e-38 scale
+            x[:, h, :] = col.reshape(rows, d)
+        t.copy_(torch.from_numpy(x).to(torch.bfloat16))
+    _check(case, gpu)
