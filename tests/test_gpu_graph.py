@@ -1,0 +1,76 @@
+"""The paged decode and the mixed varlen call inside a captured HIP graph: the library allocates
+nothing, never synchronises and records no memset, so a serving loop can capture a step once and
+replay it. Each replay runs on new query values written into the captured input buffer, with eager
+work in between, and must equal the eager call on the same inputs bit for bit."""
+
+import pytest
+import torch
+
+import attention_gqa_flash_02_amd as lib
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _to(case, dev):
+    for name, val in list(vars(case).items()):
+        if isinstance(val, torch.Tensor):
+            setattr(case, name, val.to(dev))
+    return case
+
+
+def _replays_match(call, case, out, lse, gpu):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cpu").manual_seed(9)
+    for rep in range(4):
+        case.q.copy_(torch.randn(case.q.shape, generator=gen).to(torch.bfloat16).to(gpu))
+        graph.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = out.clone(), lse.clone()
+        _ = torch.randn(1 << 20, device=gpu).sum()  # unrelated eager work between replays
+        call()                                       # eager, same inputs
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, out), f"replay {rep}: output differs from the eager call"
+        assert torch.equal(got_l, lse), f"replay {rep}: lse differs from the eager call"
+
+
+def test_decode_in_graph(gpu):
+    case = _to(synth.config_case("c2", shrink=4), gpu)
+    b, hq, d = case.q.shape
+    out = torch.empty_like(case.q)
+    lse = torch.empty((b, hq), dtype=torch.float32, device=gpu)
+    splits = lib.attn_decode_num_splits(b, case.num_kv_heads, d, 0, case.block_size, case.block_table.shape[1], 0)
+    ws = torch.empty(lib.attn_decode_workspace_bytes(b, case.num_kv_heads, d, splits), dtype=torch.uint8,
+                     device=gpu)
+
+    def call():
+        lib.attn_decode_paged(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens_k, case.scale,
+                              out=out, lse=lse, num_splits=splits, workspace=ws)
+    _replays_match(call, case, out, lse, gpu)
+
+
+def test_mixed_in_graph(gpu):
+    case = _to(synth.config_case("c5", shrink=8), gpu)
+    t, hq, d = case.q.shape
+    b = case.seq_lens_k.numel()
+    out = torch.empty_like(case.q)
+    lse = torch.empty((t, hq), dtype=torch.float32, device=gpu)
+    splits = lib.attn_decode_num_splits(b, case.num_kv_heads, d, 1, case.block_size, case.block_table.shape[1], 0)
+    ws = torch.empty(lib.attn_varlen_workspace_bytes(b, case.num_kv_heads, d, splits), dtype=torch.uint8,
+                     device=gpu)
+    max_q = max(case.q_lens)
+
+    def call():
+        lib.attn_varlen_paged(case.q, case.k_cache, case.v_cache, case.block_table, case.cu_seqlens_q,
+                              case.seq_lens_k, case.causal, case.scale, k_scale=case.k_scale, v_scale=case.v_scale,
+                              out=out, lse=lse, max_q_len=max_q, num_splits=splits, workspace=ws)
+    _replays_match(call, case, out, lse, gpu)
