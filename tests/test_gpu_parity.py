@@ -102,6 +102,22 @@ def test_decode_workspace_reuse(gpu):
         compare(out, lse, ref_o, ref_l, label=f"workspace reuse B={case.q.shape[0]} splits={splits}")
 
 
+@pytest.mark.parametrize("kv_format", ["bf16", "e4m3fn"])
+@pytest.mark.parametrize("d,bs", [(128, 16), (128, 64), (256, 16), (256, 64), (256, 128)])
+def test_decode_every_variant(gpu, kv_format, d, bs):
+    """Every decode kernel instantiation: head_dim 128/256 x bf16/e4m3fn pages x page rows of at
+    most 32 tokens (nontemporal V loads per half) and longer ones (loads issued in pairs)."""
+    lens = [1, 31, 64, 65, 200, 700, 1500]
+    gen = torch.Generator().manual_seed(60 + d + bs)
+    case = _to(synth.make_paged(60 + d + bs, lens, [1] * len(lens), 16, 4, d, bs, kv_format=kv_format,
+                                lengths_drawn=gen), gpu)
+    tol = MAX_ABS_FP8 if kv_format == "e4m3fn" else 1e-2
+    for splits in (0, 1, 5):
+        out, lse = _run_decode(case, splits)
+        ref_o, ref_l = oracle_paged(case)
+        compare(out, lse, ref_o, ref_l, max_abs=tol, label=f"decode {kv_format} d={d} bs={bs} splits={splits}")
+
+
 @pytest.mark.parametrize("d,bs", [(256, 16), (128, 32), (128, 16)])
 def test_decode_fp8(gpu, d, bs):
     lens = [1, 15, 16, 17, 300, 1000]
@@ -147,7 +163,7 @@ def test_varlen_c5_shrunk(gpu):
 
 
 @pytest.mark.parametrize("kv_format", ["bf16", "e4m3fn"])
-@pytest.mark.parametrize("d,bs", [(128, 16), (256, 16), (128, 64)])
+@pytest.mark.parametrize("d,bs", [(128, 16), (256, 16), (128, 64), (256, 64)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_varlen_mixed(gpu, kv_format, d, bs, causal):
     # decode rows (q_len 1..4 with g = 4 stay on the decode path), prefill chunks over prefixes,
