@@ -524,30 +524,37 @@ __device__ __forceinline__ void merge_row(const PagedParams& p, int b, int kvh, 
   const int dq = tid % DQ, grp = tid / DQ;
   float M = kNegInf, S = 0.f;
   f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = grp; k0 < ns; k0 += 8 * GROUPS) {
-    float lk[8];
-    f32x4 ok[8];
+  // FULL: every share holds at least one group of 4 chunks (at least as many groups as shares),
+  // so no piece needs the 64-bit divisions of the emptiness test; the choice is uniform.
+  auto fold = [&](auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
+    for (int k0 = grp; k0 < ns; k0 += 8 * GROUPS) {
+      float lk[8];
+      f32x4 ok[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = k0 + u * GROUPS;
-      const int gk = g_lo + k;
-      const bool has = k < ns && share_start(gk, T, G) < share_start(gk + 1, T, G);
-      const size_t piece = (size_t)gk * 2 + (k == 0 ? slot_lo : 0);
-      lk[u] = has ? p.ws_lse[piece * 16 + r] : kNegInf;
-      ok[u] = has ? *reinterpret_cast<const f32x4*>(p.ws_o + (piece * 16 + r) * D + 4 * dq)
-                  : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u * GROUPS;
+        const int gk = g_lo + k;
+        const bool has = k < ns && (FULL || share_start(gk, T, G) < share_start(gk + 1, T, G));
+        const size_t piece = (size_t)gk * 2 + (k == 0 ? slot_lo : 0);
+        lk[u] = has ? p.ws_lse[piece * 16 + r] : kNegInf;
+        ok[u] = has ? *reinterpret_cast<const f32x4*>(p.ws_o + (piece * 16 + r) * D + 4 * dq)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (lk[u] == kNegInf) continue;
-      const float m2 = fmaxf(M, lk[u]);
-      const float a = (M == kNegInf) ? 0.f : fast_exp2((M - m2) * kLog2e);
-      const float w = fast_exp2((lk[u] - m2) * kLog2e);
-      S = S * a + w;
-      O = O * a + ok[u] * w;
-      M = m2;
+      for (int u = 0; u < 8; ++u) {
+        if (lk[u] == kNegInf) continue;
+        const float m2 = fmaxf(M, lk[u]);
+        const float a = (M == kNegInf) ? 0.f : fast_exp2((M - m2) * kLog2e);
+        const float w = fast_exp2((lk[u] - m2) * kLog2e);
+        S = S * a + w;
+        O = O * a + ok[u] * w;
+        M = m2;
+      }
     }
-  }
+  };
+  if ((T + 3) / 4 >= G) fold(std::true_type{});
+  else fold(std::false_type{});
   float* gstat = lds;                                  // [GROUPS][2]: maximum, sum
   float* gout = lds + 2 * GROUPS;                      // [GROUPS][D]
   if (dq == 0) {
