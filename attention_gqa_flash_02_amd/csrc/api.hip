@@ -216,6 +216,7 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   p.Hkv = num_kv_heads;
   p.g = g;
   p.bs = block_size;
+  p.bs_shift = __builtin_ctz((unsigned)block_size);
   p.max_blocks = max_blocks_per_seq;
   p.num_wg = S;
   p.causal = 1;
@@ -275,6 +276,7 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
   dp.Hkv = num_kv_heads;
   dp.g = g;
   dp.bs = block_size;
+  dp.bs_shift = __builtin_ctz((unsigned)block_size);
   dp.max_blocks = max_blocks_per_seq;
   dp.num_wg = S;
   dp.causal = causal;

@@ -65,6 +65,7 @@ struct PagedParams {
   float scale;
   int num_seqs, Hq, Hkv, g, bs, max_blocks, num_wg, causal;
   int window;                  // > 0: row i of a request also drops keys j < len - qlen + i - window + 1
+  int bs_shift;                // log2(bs): block sizes are powers of two
 };
 
 // First key any row of a request with qlen new rows and len keys may see (the sliding window's
@@ -191,10 +192,13 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
   // A K lane j loads the run of quad j/4, a V lane the run of its own quad. Runs past the end of
   // the request read its last page instead (and are masked). Within a page the run starts at
   // slot (T0 + 32h) % bs + 8q % bs (T0 is a multiple of 64 and bs of 16).
-  const int kq8 = (8 * (j >> 2)) % p.bs;
-  const int vq8 = (8 * qd) % p.bs;
-  auto k_block = [&](int T0, int h) { return min(T0 + 32 * h + 8 * (j >> 2), last_tok) / p.bs; };
-  auto v_block = [&](int T0, int h) { return min(T0 + 32 * h + 8 * qd, last_tok) / p.bs; };
+  // token -> (page, slot) by shift and mask (block sizes are powers of two; every token index
+  // here is non-negative)
+  const int bmask = p.bs - 1;
+  const int kq8 = (8 * (j >> 2)) & bmask;
+  const int vq8 = (8 * qd) & bmask;
+  auto k_block = [&](int T0, int h) { return min(T0 + 32 * h + 8 * (j >> 2), last_tok) >> p.bs_shift; };
+  auto v_block = [&](int T0, int h) { return min(T0 + 32 * h + 8 * qd, last_tok) >> p.bs_shift; };
 
   int T0 = (kc0 + c0 + wave_first) * CH;
   int kphys[NH], vphys[NH];
@@ -215,7 +219,7 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
     u32x4 kraw[NU][KW];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const int kslot = (T0 + 32 * h) % p.bs + kq8;     // an 8-token run never crosses a page
+      const int kslot = ((T0 + 32 * h) & bmask) + kq8;  // an 8-token run never crosses a page
       const char* krun = kc + (size_t)kphys[h] * block_stride + (size_t)kslot * D * ELT;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -234,7 +238,7 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
     const char* vrun[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const int vslot = (T0 + 32 * h) % p.bs + vq8;
+      const int vslot = ((T0 + 32 * h) & bmask) + vq8;
       vrun[h] = vc + (size_t)vphys[h] * block_stride + ((size_t)j * p.bs + vslot) * ELT;
     }
     auto vload = [&](int h, int n, bool nt) {
