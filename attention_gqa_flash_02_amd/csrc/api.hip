@@ -301,6 +301,7 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
   pp.hpw = gcd_int(g, 4);
   pp.causal = causal;
   pp.bs = block_size;
+  pp.bs_shift = __builtin_ctz((unsigned)block_size);
   pp.max_blocks = max_blocks_per_seq;
   hipError_t e = launch_mixed(pp, dp, head_dim, kvt, total_q, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;

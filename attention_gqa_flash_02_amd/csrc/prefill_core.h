@@ -71,6 +71,7 @@ struct PrefillParams {
   float scale;
   int num_seqs, Hq, Hkv, g, hpw, causal, num_qtiles, bs, max_blocks;
   int window;                  // > 0: row i also drops keys j < shift + i - window + 1
+  int bs_shift;                // log2(bs) for paged K/V: block sizes are powers of two
 };
 
 template <int D, int BN>
@@ -191,7 +192,7 @@ struct PagedLoader {
   const char* vc;
   const int32_t* table;
   size_t block_stride;                              // bytes between consecutive blocks
-  int Lk, bs;
+  int Lk, bs, bs_shift;
 
   __device__ __forceinline__ void init(const PrefillParams& p, int b, int kvh, int Lk_, int first_tile) {
     const size_t page = (size_t)p.bs * D * ELT;
@@ -201,6 +202,7 @@ struct PagedLoader {
     table = p.block_table + (size_t)b * p.max_blocks;
     Lk = Lk_;
     bs = p.bs;
+    bs_shift = p.bs_shift;
     if (first_tile * BN < Lk) load_table(first_tile);
   }
   // Block-table entries are loaded one tile ahead of the K/V loads that use them, so a fetch
@@ -212,11 +214,11 @@ struct PagedLoader {
     const int n0 = n * BN;
     const int last = Lk - 1;
 #pragma unroll
-    for (int it = 0; it < K_LOADS; ++it) kphys[it] = table[min(n0 + (it * 256 + tid) / K_CH, last) / bs];
+    for (int it = 0; it < K_LOADS; ++it) kphys[it] = table[min(n0 + (it * 256 + tid) / K_CH, last) >> bs_shift];
 #pragma unroll
     for (int it = 0; it < V_LOADS; ++it) {
       const int t0 = n0 + VPL * ((it * 256 + tid) % V_CH);
-      vphys[it] = table[min(t0, last & ~(VPL - 1)) / bs];
+      vphys[it] = table[min(t0, last & ~(VPL - 1)) >> bs_shift];
     }
   }
   __device__ __forceinline__ void fetch(int n) {                // table entries of tile n are loaded
@@ -228,7 +230,7 @@ struct PagedLoader {
     for (int it = 0; it < K_LOADS; ++it) {
       const int idx = it * 256 + tid;
       const int key = min(n0 + idx / K_CH, last), ch = idx % K_CH;
-      const char* row = kc + (size_t)kphys[it] * block_stride + (size_t)(key % bs) * D * ELT;
+      const char* row = kc + (size_t)kphys[it] * block_stride + (size_t)(key & (bs - 1)) * D * ELT;
       kreg[it] = ld16(row + 16 * ch);                 // rows past the keys are zeroed in stage
     }
 #pragma unroll
@@ -236,7 +238,7 @@ struct PagedLoader {
       const int idx = it * 256 + tid;
       const int d = idx / V_CH, t0 = n0 + VPL * (idx % V_CH);
       const int tt = min(t0, last & ~(VPL - 1));          // a VPL-aligned run inside a valid page
-      vreg[it] = ld16(vc + (size_t)vphys[it] * block_stride + ((size_t)d * bs + tt % bs) * ELT);
+      vreg[it] = ld16(vc + (size_t)vphys[it] * block_stride + ((size_t)d * bs + (tt & (bs - 1))) * ELT);
     }
     if ((n + 1) * BN < Lk) load_table(n + 1);
   }
