@@ -25,12 +25,13 @@
 // Loads past the request's last key read zero (range-checked buffer resource).
 //
 // Schedule, with m = tile index counted from the first tile the workgroup sees:
-//   slot 2m:   A: P V (m-1), S^T (m)        B: issue batch m+1, then softmax (m-1)
-//   slot 2m+1: A: softmax (m)               B: P V (m-1), S^T (m), then wait for batch m
-// Batch j holds the loads of K (j+1) and V (j). K and V have three LDS buffers each (tile n in
-// buffer n mod 3), so batch j, issued in slot 2j-2, overwrites K (j-2) and V (j-3), both last
-// read in slot 2j-3, and is waited for at the end of slot 2j+1, before its first read in slot
-// 2j+2: a load has four slots of latency. Every wave runs every tile of its workgroup:
+//   slot 2m:   A: P V (m-1), S^T (m)        B: issue V (m+2), then softmax (m-1)
+//   slot 2m+1: A: issue K (m+2), softmax(m) B: P V (m-1), S^T (m), then wait for V (m)
+// and A waits for K (m+1) at the end of slot 2m+1. K and V have three LDS buffers each (tile n in
+// buffer n mod 3): V (j) goes out in slot 2j-2 and K (j+1) in slot 2j-1, each overwriting a tile
+// last read in slot 2j-3, and both are waited for before the barrier that ends slot 2j+1, ahead
+// of their first read in slot 2j+2. Each group issues one tile's loads, so the data lands in two
+// smaller bursts. Every wave runs every tile of its workgroup:
 // tiles that a wave's rows do not see are masked. The control flow is therefore uniform, and every
 // slot runs the same straight-line MFMA stream.
 #pragma once
@@ -335,14 +336,19 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
   // runs slots 2m+1 (matrix) and 2m+2 (softmax), and it issues the tile loads of every even slot 2j
   // (K j+1 and V j) at its start and waits for them at the end of slot 2j+1. The matrix work runs
   // at a raised wave priority, so that the SIMD's other wave never holds up an MFMA's issue.
-  auto issue_loads = [&](int j, auto jb_c) {
-    constexpr int JB = decltype(jb_c)::value;          // j % NBUF
+  // K (j+1) into buffer (j+1) mod NBUF, issued by group A; V (j) into buffer j mod NBUF, issued
+  // by group B. Each wave writes the 1 KB blocks LPW*lw .. of the tile.
+  auto issue_k = [&](int j, auto kb_c) {
+    constexpr int KB = decltype(kb_c)::value;          // (j + 1) % NBUF
     const u32x4 rk = tile_rsrc(kbase, n_first + j + 1, j + 1 < N);
-    const u32x4 rv = tile_rsrc(vbase, n_first + j, j < N);
-    unsigned char* kdst = kbuf0 + ((JB + 1) % NBUF) * S::TILE + 1024 * LPW * lw;
-    unsigned char* vdst = vbuf0 + JB * S::TILE + 1024 * LPW * lw;
+    unsigned char* kdst = kbuf0 + KB * S::TILE + 1024 * LPW * lw;
 #pragma unroll
     for (int q = 0; q < LPW; ++q) load_block(rk, koff[q], kdst + 1024 * q);
+  };
+  auto issue_v = [&](int j, auto vb_c) {
+    constexpr int VB = decltype(vb_c)::value;          // j % NBUF
+    const u32x4 rv = tile_rsrc(vbase, n_first + j, j < N);
+    unsigned char* vdst = vbuf0 + VB * S::TILE + 1024 * LPW * lw;
 #pragma unroll
     for (int q = 0; q < LPW; ++q) load_block(rv, voff[q], vdst + 1024 * q);
   };
@@ -350,14 +356,23 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
+  static_assert(LPW == 4, "a group's batch is 4 loads per wave (the vmcnt below)");
   if (gp == 0) {
+    // K (j+1) goes out at the start of slot 2j-1 (K 1 before slot 0) and is waited for at the end
+    // of slot 2j+1; it overwrites K (j-2), last read in slot 2j-3, and is first read in slot 2j+2.
+    issue_k(0, I1{});
     auto step = [&](int m, auto kb_c) {
+      constexpr int KB = decltype(kb_c)::value;
       if (m > N) return;
       __builtin_amdgcn_s_setprio(1);
       matrix_slot(kb_c);
       __builtin_amdgcn_s_setprio(0);
       __syncthreads();
+      if (m + 1 <= N) issue_k(m + 1, std::integral_constant<int, (KB + 2) % 3>{});
       if (m < N) softmax_work(m);
+      // wait for K (m+1) only: K (m+2), issued after it, may stay in flight
+      if (m + 1 <= N) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     };
     for (int m = 0; m <= N; m += 3) {
@@ -367,12 +382,11 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
     }
     __syncthreads();
   } else {
-    // Batch j = the loads of K (j+1) and V (j). Batches 0 and 1 go out in slot 0; batch m+2 goes
-    // out at the start of slot 2m+2 and batch m is waited for at the end of slot 2m+1, so a load
-    // has four slots of latency.
-    static_assert(2 * LPW == 8, "a batch is 8 loads per wave (the vmcnt below)");
-    issue_loads(0, I0{});
-    if (1 <= N) issue_loads(1, I1{});
+    // V (j) goes out at the start of slot 2j-2 (V 0 and V 1 in slot 0) and is waited for at the
+    // end of slot 2j+1; it overwrites V (j-3), last read in slot 2j-3, and is first read in slot
+    // 2j+2.
+    issue_v(0, I0{});
+    if (1 <= N) issue_v(1, I1{});
     __syncthreads();
     auto step = [&](int m, auto kb_c) {
       constexpr int KB = decltype(kb_c)::value;
@@ -380,11 +394,11 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
       __builtin_amdgcn_s_setprio(1);
       matrix_slot(kb_c);
       __builtin_amdgcn_s_setprio(0);
-      // wait for batch m only: batch m+1, issued after it, may stay in flight
-      if (m + 1 <= N) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      // wait for V (m) only: V (m+1), issued after it, may stay in flight
+      if (m + 1 <= N) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (m + 2 <= N) issue_loads(m + 2, std::integral_constant<int, (KB + 2) % 3>{});
+      if (m + 2 <= N) issue_v(m + 2, std::integral_constant<int, (KB + 2) % 3>{});
       if (m < N) softmax_work(m);
       __syncthreads();
     };
