@@ -25,7 +25,7 @@
 // Loads past the request's last key read zero (range-checked buffer resource).
 //
 // Schedule, with m = tile index counted from the first tile the workgroup sees:
-//   slot 2m:   A: P V (m-1), S^T (m)        B: issue V (m+2), then softmax (m-1)
+//   slot 2m:   A: P V (m-1), S^T (m)        B: issue V (m+1), then softmax (m-1)
 //   slot 2m+1: A: issue K (m+2), softmax(m) B: P V (m-1), S^T (m), then wait for V (m)
 // and A waits for K (m+1) at the end of slot 2m+1. K and V have three LDS buffers each (tile n in
 // buffer n mod 3): V (j) goes out in slot 2j-2 and K (j+1) in slot 2j-1, each overwriting a tile
