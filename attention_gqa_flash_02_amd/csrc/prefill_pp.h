@@ -115,9 +115,9 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
   const int lower = win > 0 ? qrow_i - win + 1 : INT_MIN;
   const int wave_mask_from = p.causal ? max(0, tw + 1) : Lk;
 
-  // ---- tile loads, all issued by group B: its wave w (0-3) fills 1 KB blocks LPW*w .. of each K
-  // and V tile; lane l of a block writes slot l & 15 of row 4 * block + l / 16, i.e. it loads
-  // global chunk slot ^ swz(row) of that row
+  // ---- tile loads: group A loads the K tiles and group B the V tiles (and the first K tile); wave
+  // w of a group (0-3) fills 1 KB blocks LPW*w .. of the tile; lane l of a block writes slot l & 15
+  // of row 4 * block + l / 16, i.e. it loads global chunk slot ^ swz(row) of that row
   const long long stride = (long long)p.Hkv * D;
   const long long row_bytes = stride * 2;
   const char* kbase = reinterpret_cast<const char*>(p.k + (size_t)q0 * stride + (size_t)kvh * D);
@@ -333,9 +333,9 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
       pedge = edge;
   };
   // Group A runs slots 2m (matrix) and 2m+1 (softmax) in iteration m; group B, one slot later,
-  // runs slots 2m+1 (matrix) and 2m+2 (softmax), and it issues the tile loads of every even slot 2j
-  // (K j+1 and V j) at its start and waits for them at the end of slot 2j+1. The matrix work runs
-  // at a raised wave priority, so that the SIMD's other wave never holds up an MFMA's issue.
+  // runs slots 2m+1 (matrix) and 2m+2 (softmax). Each group issues its tile's loads at the start
+  // of its softmax slot (see the schedule at the top). The matrix work runs at a raised wave
+  // priority, so that the SIMD's other wave never holds up an MFMA's issue.
   // K (j+1) into buffer (j+1) mod NBUF, issued by group A; V (j) into buffer j mod NBUF, issued
   // by group B. Each wave writes the 1 KB blocks LPW*lw .. of the tile.
   auto issue_k = [&](int j, auto kb_c) {
