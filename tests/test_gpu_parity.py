@@ -204,3 +204,16 @@ def test_varlen_multi_token_decode(gpu, hq, hkv):
         out, lse = _run_varlen(case, splits)
         ref_o, ref_l = oracle_paged(case)
         compare(out, lse, ref_o, ref_l, label=f"multi-token hq={hq} hkv={hkv} splits={splits}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_many_key_tiles(gpu, hq, hkv, causal):
+    """Requests of 4 to 12 key tiles of 64, so that the ping-pong loop (unrolled by three over its
+    three tile buffers) ends at every position of its unroll, with and without the causal mask, for
+    query tiles of 64 rows (4 heads per workgroup) and 256 rows (one head per workgroup)."""
+    lens = [257, 300, 384, 449, 520, 640, 700, 767]
+    case = _to(synth.make_prefill(500 + hq + int(causal), lens, hq, hkv, 128, causal=causal), gpu)
+    out, lse = _run_prefill(case)
+    ref_o, ref_l = oracle_prefill(case)
+    compare(out, lse, ref_o, ref_l, label=f"many tiles hq={hq} hkv={hkv} causal={causal}")
