@@ -167,3 +167,21 @@ def test_append_validation(kw, code):
 def test_append_nothing_is_a_noop():
     assert _append(total=0) == 0
     assert _append(total=0, kn=None, vn=None) == 0
+
+
+def test_missing_library_raises_and_nothing_falls_back(monkeypatch, tmp_path):
+    """Without the built library every entry point raises; no other implementation answers."""
+    import torch
+    import attention_gqa_flash_02_amd as attn
+
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libattn_gqa.so"))
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.load()
+    q = torch.zeros(16, 4, 128, dtype=torch.bfloat16)
+    kv = torch.zeros(16, 1, 128, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 16], dtype=torch.int32)
+    with pytest.raises(_lib.LibraryMissing):
+        attn.attn_prefill_varlen(q, kv, kv, cu, True, 128 ** -0.5, max_seqlen=16)
+    with pytest.raises(_lib.LibraryMissing):
+        attn.attn_decode_workspace_bytes(2, 2, 128, 4)
