@@ -16,20 +16,28 @@ c_ip = ctypes.POINTER(ctypes.c_int32)
 
 SIGNATURES = {
     "attn_status_string": (ctypes.c_char_p, [c_i32]),
-    "attn_prefill_varlen": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_f32, c_i32, c_void_p, c_void_p,
-                                    c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_void_p]),
+    # q, k, v, cu_seqlens, causal, scale, out, lse, num_seqs, total_tokens, max_seqlen, Hq, Hkv, D, window, stream
+    "attn_prefill_varlen": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_f32, c_void_p, c_void_p,
+                                    c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_void_p]),
+    # q, k, v, q_scale, k_scale, v_scale, cu_seqlens, causal, scale, out, lse, num_seqs, total_tokens,
+    # max_seqlen, Hq, Hkv, D, window, stream
     "attn_prefill_varlen_fp8": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                        c_i32, c_f32, c_i32, c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32,
-                                        c_i32, c_i32, c_void_p]),
+                                        c_i32, c_f32, c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32,
+                                        c_i32, c_i32, c_i32, c_void_p]),
     "attn_decode_num_splits": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "attn_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32]),
-    "attn_decode_paged": (c_i32, [c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_void_p, c_void_p, c_void_p,
-                                  c_f32, c_i32, c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
-                                  c_i32, c_void_p, c_size, c_void_p]),
+    # q, k_cache, v_cache, block_table, seq_lens, scale, out, num_seqs, Hq, Hkv, D, block_size, num_blocks,
+    # max_blocks_per_seq, num_splits, lse, workspace, workspace_bytes, kv_dtype, k_scale, v_scale, window, stream
+    "attn_decode_paged": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_f32, c_void_p,
+                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_void_p,
+                                  c_void_p, c_size, c_i32, c_void_p, c_void_p, c_i32, c_void_p]),
     "attn_varlen_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32]),
+    # q, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_table, cu_seqlens_q, seq_lens_k, causal, scale,
+    # out, lse, num_seqs, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
+    # num_splits, workspace, workspace_bytes, window, stream
     "attn_varlen_paged": (c_i32, [c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_void_p, c_void_p, c_void_p,
-                                  c_void_p, c_i32, c_f32, c_i32, c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
-                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_void_p, c_size, c_void_p]),
+                                  c_void_p, c_i32, c_f32, c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_void_p, c_size, c_i32, c_void_p]),
     "attn_kv_append_paged": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                      c_void_p]),

@@ -10,13 +10,28 @@
 
 namespace attn {
 
-int device_cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+int current_device_index() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
-    return 256;
+    return -1;
   }
+  return (dev >= 0 && dev < kMaxDevices) ? dev : -1;
+}
+
+hipError_t ensure_dynamic_lds(const void* kernel, std::atomic<bool>* done, int bytes) {
+  const int dev = current_device_index();
+  if (dev >= 0 && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  if (dev >= 0) done[dev].store(true, std::memory_order_release);
+  return hipSuccess;
+}
+
+int device_cu_count() {
+  static std::atomic<int> cache[kMaxDevices];
+  const int dev = current_device_index();
+  if (dev < 0) return 256;
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
   int cus = 0;
@@ -41,12 +56,6 @@ static int gcd_int(int a, int b) {
   return a;
 }
 
-// Upper bound on decode partitions (it bounds the workspace: two partial slots per partition).
-constexpr int kMaxSplits = 4096;
-// Upper bound on requests of a paged call: the partition kernel keeps one chunk offset per
-// request in LDS.
-constexpr int kMaxPagedSeqs = 16384;
-
 
 }  // namespace attn
 
@@ -67,9 +76,9 @@ const char* attn_status_string(attn_status status) {
 }
 
 attn_status attn_prefill_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
-                                int32_t causal, float scale, int32_t window, void* out, float* lse, int32_t num_seqs,
+                                int32_t causal, float scale, void* out, float* lse, int32_t num_seqs,
                                 int32_t total_tokens, int32_t max_seqlen, int32_t num_q_heads,
-                                int32_t num_kv_heads, int32_t head_dim, void* stream) {
+                                int32_t num_kv_heads, int32_t head_dim, int32_t window, void* stream) {
   if (num_seqs <= 0 || total_tokens < 0 || max_seqlen < 0 || max_seqlen > total_tokens ||
       num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
       (causal != 0 && causal != 1) || !(std::isfinite(scale) && scale >= 0.f) || window < 0)
@@ -100,9 +109,10 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v, con
 
 attn_status attn_prefill_varlen_fp8(const void* q, const void* k, const void* v, const float* q_scale,
                                     const float* k_scale, const float* v_scale, const int32_t* cu_seqlens,
-                                    int32_t causal, float scale, int32_t window, void* out, float* lse,
+                                    int32_t causal, float scale, void* out, float* lse,
                                     int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
-                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, void* stream) {
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                                    void* stream) {
   if (num_seqs <= 0 || total_tokens < 0 || max_seqlen < 0 || max_seqlen > total_tokens ||
       num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
       (causal != 0 && causal != 1) || !(std::isfinite(scale) && scale >= 0.f) || window < 0)
@@ -150,9 +160,9 @@ int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t h
   return (int32_t)(s < 1 ? 1 : s);
 }
 
-size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t num_splits) {
-  if (num_seqs <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
   return (size_t)num_splits * 2 * 16 * ((size_t)head_dim + 1) * sizeof(float) +
          ((size_t)num_seqs + 1) * sizeof(int32_t);
 }
@@ -176,13 +186,14 @@ static attn_status validate_paged(const void* q, const void* k_cache, const void
   return ATTN_OK;
 }
 
-attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
-                              const float* k_scale, const float* v_scale, const int32_t* block_table,
-                              const int32_t* seq_lens, float scale, int32_t window, void* out, float* lse,
+attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, float scale, void* out,
                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                              int32_t max_blocks_per_seq, int32_t num_splits, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              int32_t max_blocks_per_seq, int32_t num_splits, float* lse,
+                              void* workspace, size_t workspace_bytes,
+                              int32_t kv_dtype, const float* k_scale, const float* v_scale, int32_t window,
+                              void* stream) {
   attn_status st = validate_paged(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_table, seq_lens,
                                   out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                   num_blocks, max_blocks_per_seq, num_splits);
@@ -192,7 +203,7 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   if (g > 16) return ATTN_ERR_UNSUPPORTED;
   const int S = attn_decode_num_splits(num_seqs, num_kv_heads, head_dim, kv_dtype, block_size,
                                        max_blocks_per_seq, num_splits);
-  const size_t need = attn_decode_workspace_bytes(num_seqs, num_kv_heads, head_dim, S);
+  const size_t need = attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, S);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
 
   PagedParams p{};
@@ -225,18 +236,19 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-size_t attn_varlen_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+size_t attn_varlen_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t num_splits) {
-  return attn_decode_workspace_bytes(num_seqs, num_kv_heads, head_dim, num_splits);
+  return attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, num_splits);
 }
 
 attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
                               const float* k_scale, const float* v_scale, const int32_t* block_table,
                               const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t causal,
-                              float scale, int32_t window, void* out, float* lse, int32_t num_seqs, int32_t total_q,
+                              float scale, void* out, float* lse, int32_t num_seqs, int32_t total_q,
                               int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                              int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+                              int32_t num_splits, void* workspace, size_t workspace_bytes, int32_t window,
+                              void* stream) {
   attn_status st = validate_paged(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_table, seq_lens_k,
                                   out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                   num_blocks, max_blocks_per_seq, num_splits);
@@ -249,7 +261,7 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
   if (num_seqs > mixed_max_seqs(head_dim)) return ATTN_ERR_UNSUPPORTED;
   const int S = attn_decode_num_splits(num_seqs, num_kv_heads, head_dim, kv_dtype, block_size,
                                        max_blocks_per_seq, num_splits);
-  const size_t need = attn_varlen_workspace_bytes(num_seqs, num_kv_heads, head_dim, S);
+  const size_t need = attn_varlen_workspace_bytes(num_seqs, num_q_heads, head_dim, S);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (total_q == 0) return ATTN_OK;
   const int g = num_q_heads / num_kv_heads;

@@ -177,8 +177,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
 template <int D, bool FP8>
 static hipError_t launch_append_t(const AppendParams& p, hipStream_t stream) {
   dim3 grid((p.total_new + kAppendRows - 1) / kAppendRows, p.Hkv);
-  hipLaunchKernelGGL((kv_append_kernel<D, FP8>), grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(&kv_append_kernel<D, FP8>, grid, dim3(256), 0, stream, p);
 }
 
 hipError_t launch_append(const AppendParams& p, int head_dim, int kv_type, hipStream_t stream) {

@@ -34,9 +34,6 @@ constexpr int kBufferFlags = 0x00020000;
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -63,11 +60,6 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 
 __device__ __forceinline__ bf16x4 f32x4_to_bf16x4(f32x4 x) {
   return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
-}
-
-// Sum of the two bf16 values of v added to acc in fp32 (one v_dot2_f32_bf16 against (1, 1)).
-__device__ __forceinline__ float add_bf16x2(bf16x2 v, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(v, bf16x2{(bf16)1.0f, (bf16)1.0f}, acc, false);
 }
 
 // max(a, b, c) in one v_max3_f32.

@@ -15,39 +15,61 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(PagedParams p) {
   merge_row<D, CH>(p, blockIdx.z, blockIdx.y, blockIdx.x, reinterpret_cast<float*>(smem_raw));
 }
 
+// Dynamic LDS of the partition kernel: 128 floats of statistics and four waves' O rows, then the
+// chunk prefix sums (num_seqs + 1) and 4 scratch ints.
+template <int D>
+static size_t decode_lds_bytes(int rows_max, int num_seqs) {
+  return (size_t)(128 + 4 * rows_max * D) * sizeof(float) + ((size_t)num_seqs + 5) * sizeof(int);
+}
+
+template <int D>
+static size_t merge_lds_bytes() {
+  return (size_t)(256 / (D / 4)) * (D + 2) * sizeof(float);
+}
+
+template <int D, int CH>
+static hipError_t ensure_merge_t() {
+  static std::atomic<bool> done[kMaxDevices];
+  return ensure_dynamic_lds(reinterpret_cast<const void*>(&decode_merge_kernel<D, CH>), done,
+                            (int)merge_lds_bytes<D>());
+}
+
+hipError_t ensure_merge_attrs(int head_dim, int nu) {
+  if (head_dim == 128 && nu == 4) return ensure_merge_t<128, 64>();
+  if (head_dim == 128 && nu == 2) return ensure_merge_t<128, 32>();
+  if (head_dim == 256 && nu == 4) return ensure_merge_t<256, 64>();
+  if (head_dim == 256 && nu == 2) return ensure_merge_t<256, 32>();
+  return hipErrorInvalidValue;
+}
+
+// The dynamic-LDS limits of the partition kernel (its largest launch: 16 rows, the most requests a
+// paged call takes) and of the merge kernel, raised once per device before either is launched.
+template <int D, int KVT, int NU, bool LONGV>
+static hipError_t ensure_decode_attrs() {
+  static std::atomic<bool> done[kMaxDevices];
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&decode_share_kernel<D, KVT, NU, LONGV>),
+                                    done, (int)decode_lds_bytes<D>(16, kMaxPagedSeqs));
+  if (e != hipSuccess) return e;
+  return ensure_merge_t<D, DecodeShape<NU>::CH>();
+}
+
 template <int D, int KVT, int NU, bool LONGV>
 static hipError_t launch_decode_t(const PagedParams& p, int rows_max, hipStream_t stream) {
-  // partition kernel LDS: 128 floats of statistics, four waves' O rows, then the chunk prefix
-  // sums and 4 scratch ints
+  hipError_t e = ensure_decode_attrs<D, KVT, NU, LONGV>();
+  if (e != hipSuccess) return e;
   const int combine_floats = 128 + 4 * rows_max * D;
-  const size_t lds = (size_t)combine_floats * sizeof(float) + ((size_t)p.num_seqs + 5) * sizeof(int);
-  // the dynamic-LDS limit of each kernel is raised to the largest size launched so far
-  static size_t lds_set = 0;
-  if (lds > lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_share_kernel<D, KVT, NU, LONGV>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    lds_set = lds;
-  }
-  hipLaunchKernelGGL((decode_share_kernel<D, KVT, NU, LONGV>), dim3(p.num_wg), dim3(256), lds, stream, p, combine_floats);
-  hipError_t e = hipGetLastError();
+  e = launch_kernel(&decode_share_kernel<D, KVT, NU, LONGV>, dim3(p.num_wg), dim3(256),
+                    decode_lds_bytes<D>(rows_max, p.num_seqs), stream, p, combine_floats);
   if (e != hipSuccess) return e;
   return launch_decode_merge(p, D, NU, rows_max, stream);
 }
 
 template <int D, int CH>
 static hipError_t launch_merge_t(const PagedParams& p, int rows_max, hipStream_t stream) {
-  const size_t merge_lds = (size_t)(256 / (D / 4)) * (D + 2) * sizeof(float);
-  static size_t merge_lds_set = 0;
-  if (merge_lds > merge_lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_merge_kernel<D, CH>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)merge_lds);
-    if (e != hipSuccess) return e;
-    merge_lds_set = merge_lds;
-  }
+  hipError_t e = ensure_merge_t<D, CH>();
+  if (e != hipSuccess) return e;
   dim3 mgrid(rows_max, p.Hkv, p.num_seqs);
-  hipLaunchKernelGGL((decode_merge_kernel<D, CH>), mgrid, dim3(256), merge_lds, stream, p);
-  return hipGetLastError();
+  return launch_kernel(&decode_merge_kernel<D, CH>, mgrid, dim3(256), merge_lds_bytes<D>(), stream, p);
 }
 
 hipError_t launch_decode_merge(const PagedParams& p, int head_dim, int nu, int rows_max, hipStream_t stream) {
@@ -80,10 +102,14 @@ int decode_chunk_tokens(int head_dim, int kv_type) {
 template <int D, int KVT, int NU>
 static int wgs_per_cu_t() {
   // Resident partition workgroups per compute unit (the register-limited occupancy of the
-  // variant; the smaller of its two V-load forms), queried once; a failed query leaves no
-  // pending error and counts as 1.
-  static int cached = 0;
-  if (cached > 0) return cached;
+  // variant; the smaller of its two V-load forms), queried once per device; a failed query
+  // leaves no pending error and counts as 1.
+  static std::atomic<int> cache[kMaxDevices];
+  const int dev = current_device_index();
+  if (dev >= 0) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
   int n = INT_MAX;
   for (const void* fn : {reinterpret_cast<const void*>(&decode_share_kernel<D, KVT, NU, false>),
                          reinterpret_cast<const void*>(&decode_share_kernel<D, KVT, NU, true>)}) {
@@ -94,7 +120,7 @@ static int wgs_per_cu_t() {
     }
     n = std::min(n, m);
   }
-  cached = n;
+  if (dev >= 0) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

@@ -4,11 +4,43 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "decode_core.h"
 #include "prefill_core.h"
 
 namespace attn {
+
+// Devices the per-device caches below cover (device ids 0 .. kMaxDevices - 1).
+constexpr int kMaxDevices = 64;
+// Upper bound on decode partitions (it bounds the workspace: two partial slots per partition).
+constexpr int kMaxSplits = 4096;
+// Upper bound on requests of a paged call: the partition kernel keeps one chunk offset per
+// request in LDS.
+constexpr int kMaxPagedSeqs = 16384;
+
+// The current device's id if it is in [0, kMaxDevices), else -1 (a failed query leaves no
+// pending error).
+int current_device_index();
+
+template <class T>
+struct ident {
+  using type = T;
+};
+
+// Launch a kernel with hipLaunchKernel and return that launch's own status (so an error left
+// pending by earlier, unrelated work is neither reported as this launch's nor cleared).
+template <typename... KArgs>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                         typename ident<KArgs>::type... args) {
+  void* ptrs[] = {static_cast<void*>(&args)..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, stream);
+}
+
+// Raise the dynamic-LDS limit of `kernel` to `bytes` (a constant per kernel: the most any of its
+// launches takes) once per device; `done` holds one flag per device. Setting it twice is harmless,
+// so concurrent first calls need no lock.
+hipError_t ensure_dynamic_lds(const void* kernel, std::atomic<bool>* done, int bytes);
 
 // Varlen prefill over contiguous K/V. Grid: (head groups, sequences, query tiles), query tiles
 // walked heaviest (last) first.
@@ -26,8 +58,10 @@ hipError_t launch_prefill_fp8(const PrefillFp8Params& p, int max_seqlen, hipStre
 hipError_t launch_decode(const PagedParams& p, int head_dim, int kv_type, int rows_max, hipStream_t stream);
 
 // The LSE merge alone (the second launch of a paged decode / mixed call); nu = the partition
-// kernel's sub-tiles per chunk (chunk = 16 * nu keys).
+// kernel's sub-tiles per chunk (chunk = 16 * nu keys). ensure_merge_attrs raises the merge
+// kernel's LDS limit on the current device without launching it.
 hipError_t launch_decode_merge(const PagedParams& p, int head_dim, int nu, int rows_max, hipStream_t stream);
+hipError_t ensure_merge_attrs(int head_dim, int nu);
 
 // Mixed varlen batch over a paged cache: one launch holding the decode path's p.num_wg shares
 // and the prefill q-tiles, then the merge.

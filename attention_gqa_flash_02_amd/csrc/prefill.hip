@@ -20,7 +20,7 @@ void prefill_varlen_kernel(PrefillParams p) {
 }
 
 // Varlen self-attention over contiguous K/V with head_dim 128: the ping-pong kernel (8 waves,
-// 64 KB of LDS, one workgroup per compute unit). Grid as above; a q-tile is 32 * 8 / hpw rows.
+// 96 KB of LDS: three 16 KB buffers each of K and V; one workgroup per compute unit). Grid as above; a q-tile is 32 * 8 / hpw rows.
 template <int BN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_pingpong_kernel(PrefillParams p) {
@@ -69,45 +69,55 @@ void varlen_mixed_kernel(PrefillParams pp, PagedParams dp, int n_dec,
 template <int D, int BN>
 static hipError_t launch_prefill_t(const PrefillParams& p, int max_seqlen, hipStream_t stream) {
   using S = PrefillShape<D, BN>;
-  static bool attr_set = false;  // per process; the attribute is a property of the function
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_varlen_kernel<D, BN>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> done[kMaxDevices];
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&prefill_varlen_kernel<D, BN>), done, S::LDS_BYTES);
+  if (e != hipSuccess) return e;
   const int tq = 32 * (4 / p.hpw);
   PrefillParams q = p;
   q.num_qtiles = (max_seqlen + tq - 1) / tq;
   if (q.num_qtiles <= 0) return hipSuccess;
   dim3 grid(p.Hkv * (p.g / p.hpw), p.num_seqs, q.num_qtiles);
-  hipLaunchKernelGGL((prefill_varlen_kernel<D, BN>), grid, dim3(256), S::LDS_BYTES, stream, q);
-  return hipGetLastError();
+  return launch_kernel(&prefill_varlen_kernel<D, BN>, grid, dim3(256), S::LDS_BYTES, stream, q);
 }
 
 template <int BN>
 static hipError_t launch_pingpong_t(const PrefillParams& p, int max_seqlen, hipStream_t stream) {
   using S = PingPongShape<BN>;
-  static bool attr_set = false;  // per process; the attribute is a property of the function
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pingpong_kernel<BN>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> done[kMaxDevices];
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&prefill_pingpong_kernel<BN>), done, S::LDS_BYTES);
+  if (e != hipSuccess) return e;
   const int tq = 32 * (8 / p.hpw);
   PrefillParams q = p;
   q.num_qtiles = (max_seqlen + tq - 1) / tq;
   if (q.num_qtiles <= 0) return hipSuccess;
   dim3 grid(p.Hkv * (p.g / p.hpw), p.num_seqs, q.num_qtiles);
-  hipLaunchKernelGGL((prefill_pingpong_kernel<BN>), grid, dim3(512), S::LDS_BYTES, stream, q);
-  return hipGetLastError();
+  return launch_kernel(&prefill_pingpong_kernel<BN>, grid, dim3(512), S::LDS_BYTES, stream, q);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, hipStream_t stream) {
   if (head_dim == 128) return launch_pingpong_t<64>(p, max_seqlen, stream);
   if (head_dim == 256) return launch_prefill_t<256, 64>(p, max_seqlen, stream);
   return hipErrorInvalidValue;
+}
+
+// Dynamic LDS of the mixed kernel: the larger of the prefill tile buffers and the decode combine
+// buffer, then num_seqs + 5 ints.
+template <int D, int BN>
+static size_t mixed_lds_bytes(int num_seqs) {
+  const size_t combine = (size_t)(128 + 4 * 16 * D) * sizeof(float);
+  return std::max((size_t)PrefillShape<D, BN>::LDS_BYTES, combine) + ((size_t)num_seqs + 5) * sizeof(int);
+}
+
+// Largest request count whose mixed-kernel LDS fits the 160 KB a workgroup may hold.
+constexpr long long kMaxWorkgroupLds = 160 * 1024;
+template <int D>
+static int mixed_max_seqs_t() {
+  const long long base = (long long)mixed_lds_bytes<D, 64>(0) - 5 * (long long)sizeof(int);
+  return (int)std::min<long long>((kMaxWorkgroupLds - base) / 4 - 5, kMaxPagedSeqs);
+}
+
+int mixed_max_seqs(int head_dim) {
+  return head_dim == 128 ? mixed_max_seqs_t<128>() : mixed_max_seqs_t<256>();
 }
 
 template <int D, int BN, int KVT, int NU, bool LONGV>
@@ -117,19 +127,16 @@ static hipError_t launch_mixed_t(const PrefillParams& pp, const PagedParams& dp,
   const long long n_pre = (long long)pp.Hkv * (pp.g / pp.hpw) * ((total_q + tq - 1) / tq + pp.num_seqs);
   const int n_dec = dp.num_wg;
   if (n_pre + n_dec > 0x7fffffffLL) return hipErrorInvalidValue;
+  // both kernels' LDS limits are raised before the first launch
+  static std::atomic<bool> done[kMaxDevices];
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV>), done,
+                                    (int)mixed_lds_bytes<D, BN>(mixed_max_seqs_t<D>()));
+  if (e != hipSuccess) return e;
+  e = ensure_merge_attrs(D, NU);
+  if (e != hipSuccess) return e;
   const int combine_floats = 128 + 4 * 16 * D;
-  const size_t ints = ((size_t)pp.num_seqs + 5) * sizeof(int);
-  const size_t lds = std::max((size_t)PrefillShape<D, BN>::LDS_BYTES, (size_t)combine_floats * sizeof(float)) + ints;
-  static size_t lds_set = 0;
-  if (lds > lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    lds_set = lds;
-  }
-  hipLaunchKernelGGL((varlen_mixed_kernel<D, BN, KVT, NU, LONGV>), dim3((unsigned)(n_pre + n_dec)), dim3(256), lds, stream,
-                     pp, dp, n_dec, combine_floats);
-  hipError_t e = hipGetLastError();
+  e = launch_kernel(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV>, dim3((unsigned)(n_pre + n_dec)), dim3(256),
+                    mixed_lds_bytes<D, BN>(pp.num_seqs), stream, pp, dp, n_dec, combine_floats);
   if (e != hipSuccess) return e;
   return launch_decode_merge(dp, D, NU, 16, stream);
 }
@@ -138,19 +145,6 @@ template <int D, int BN, int KVT, int NU>
 static hipError_t launch_mixed_bs(const PrefillParams& pp, const PagedParams& dp, int total_q, hipStream_t stream) {
   return dp.bs > 32 ? launch_mixed_t<D, BN, KVT, NU, true>(pp, dp, total_q, stream)
                     : launch_mixed_t<D, BN, KVT, NU, false>(pp, dp, total_q, stream);
-}
-
-// Largest request count whose mixed-kernel LDS (the larger of the prefill tile buffers and the
-// decode combine buffer, then num_seqs + 5 ints) fits the 160 KB a workgroup may hold.
-template <int D>
-static int mixed_max_seqs_t() {
-  constexpr long long kMaxLds = 160 * 1024;
-  const long long base = std::max((long long)PrefillShape<D, 64>::LDS_BYTES, (long long)(128 + 4 * 16 * D) * 4);
-  return (int)std::min<long long>((kMaxLds - base) / 4 - 5, INT_MAX);
-}
-
-int mixed_max_seqs(int head_dim) {
-  return head_dim == 128 ? mixed_max_seqs_t<128>() : mixed_max_seqs_t<256>();
 }
 
 hipError_t launch_mixed(const PrefillParams& pp, const PagedParams& dp, int head_dim, int kv_type, int total_q,

@@ -65,9 +65,6 @@ struct PrefillParams {
   const float* v_scale;        // [Hkv] (fp8) or nullptr
   const int32_t* block_table;  // [B, max_blocks]
   const int32_t* seq_lens_k;   // [B] keys per request (its Lq new tokens are the last ones)
-  // tile list of a mixed batch: prefill tile t of the launch -> request, q-tile (see
-  // prefill_tile_of); nullptr for a plain grid (x = head group, y = request, z = q-tile)
-  const int32_t* tile_prefix;  // [B + 1] prefix sums of q-tiles per request on this path
   float scale;
   int num_seqs, Hq, Hkv, g, hpw, causal, num_qtiles, bs, max_blocks;
   int window;                  // > 0: row i also drops keys j < shift + i - window + 1

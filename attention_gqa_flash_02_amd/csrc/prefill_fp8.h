@@ -203,7 +203,9 @@ __device__ __forceinline__ void prefill_fp8_body(const PrefillFp8Params& p, unsi
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   float mc = kNegInf, l = 0.f;
 
-  // LDS starts zeroed (a load past the keys leaves its slots as they were), then K of the first tile
+  // LDS starts zeroed, then K of the first tile. As in prefill_pp.h the kernel does not depend on what
+  // a range-checked load past the keys leaves in LDS (zero or an earlier tile's finite codes of the same
+  // request): those keys' scores are masked and their P is 0.
   {
     u32x4* z = reinterpret_cast<u32x4*>(smem);
     for (int i = tid; i < S::LDS_BYTES / 16; i += 512) z[i] = u32x4{0, 0, 0, 0};

@@ -20,8 +20,7 @@ hipError_t launch_prefill_fp8(const PrefillFp8Params& p, int max_seqlen, hipStre
   q.num_qtiles = (max_seqlen + tq - 1) / tq;
   if (q.num_qtiles <= 0) return hipSuccess;
   dim3 grid(p.Hkv * (p.g / p.hpw), p.num_seqs, q.num_qtiles);
-  hipLaunchKernelGGL((prefill_fp8_kernel<64>), grid, dim3(512), S::LDS_BYTES, stream, q);
-  return hipGetLastError();
+  return launch_kernel(&prefill_fp8_kernel<64>, grid, dim3(512), S::LDS_BYTES, stream, q);
 }
 
 }  // namespace attn

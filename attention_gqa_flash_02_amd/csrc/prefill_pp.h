@@ -22,7 +22,11 @@
 //   * V is read with the gfx950 transposing LDS read ds_read_b64_tr_b16 (within 16 lanes, lane
 //     4a + b returns element b of the 8-byte rows that lanes a, a+4, a+8 and a+12 point at). That
 //     is 4 keys x 4 chunks per 32 lanes: swz = 4 (r mod 4) + (r / 4) mod 4.
-// Loads past the request's last key read zero (range-checked buffer resource).
+// Loads past the request's last key are range-checked (the buffer resource of a tile ends at the
+// request's last key). The kernel does not depend on what such a lane leaves in LDS (zero, or the
+// bytes already there): LDS is zeroed once before the first tile, so a slot past the keys holds
+// either zero or a key of an earlier tile of the same request. Its score is masked (P = 0) and
+// 0 times a finite value adds nothing, so the only requirement is the caller's: finite K and V.
 //
 // Schedule, with m = tile index counted from the first tile the workgroup sees:
 //   slot 2m:   A: P V (m-1), S^T (m)        B: issue V (m+1), then softmax (m-1)
@@ -136,7 +140,7 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
   constexpr int NBUF = S::NBUF;
   unsigned char* const kbuf0 = smem;
   unsigned char* const vbuf0 = smem + NBUF * S::TILE;
-  // Buffer resource of tile n (no bytes when the tile does not exist: its loads then read zero).
+  // Buffer resource of tile n (no bytes when the tile does not exist: its loads fetch nothing).
   auto tile_rsrc = [&](const char* base, int n, bool exists) -> u32x4 {
     const long long t = (long long)n * BN * row_bytes;
     long long left = exists ? end_bytes - t : 0;
@@ -190,7 +194,7 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   float mc = kNegInf, l = 0.f;
 
-  // LDS starts zeroed (a load past the keys leaves its slots as they were), then K of the first tile.
+  // LDS starts zeroed (see the top of the file for the slots past the keys), then K of the first tile.
   // The Q loads, issued first, are waited for only here, together with that tile, so the two
   // latencies overlap. An empty asm then redefines the Q registers, so the tile loop never waits on
   // the memory counter for them (which would also wait for the tile loads in flight).

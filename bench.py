@@ -46,10 +46,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # The GPU raises its clocks over the first 20-40 ms of sustained load: the default warm-up runs
-    # each workload for about 50 ms before its timed calls (400 calls of the 0.13 ms decode; the
-    # millisecond-scale sections take warmup // 20 calls).
-    ap.add_argument("--warmup", type=int, default=400)
+    # Untimed calls before each section's timed ones; whatever this says, every section also warms
+    # up for at least WARM_MS of GPU time (the clocks rise over the first 20-40 ms of load).
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--splits", type=int, default=0, help="decode partitions (0 = library choice)")
     ap.add_argument("--only", choices=["c1", "c2", "c3", "c3fp8", "c4", "c5", "append"], default=None,
                     help="time one workload only (for profiling); the JSON line still names c2's metric")
@@ -81,28 +80,150 @@ def measured_traffic(key, sources):
     return entry.get("hbm_bytes_per_call")
 
 
+# The GPU raises its clocks over the first 20-40 ms of sustained load, so every section runs its
+# workload for at least this long (and at least --warmup calls) before the timed calls.
+WARM_MS = 50.0
+
+
+class GpuClock:
+    """Reads the graphics clock of the benchmarked GPU through amdsmi (matched to torch's device by
+    PCI bus id), on a background thread while a section warms up. Any failure leaves it disabled
+    and is reported instead of a clock."""
+
+    def __init__(self, dev_index=0):
+        self.handle = None
+        self.error = None
+        try:
+            import amdsmi
+            import torch
+            self.amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            props = torch.cuda.get_device_properties(dev_index)
+            want = (getattr(props, "pci_domain_id", 0), getattr(props, "pci_bus_id", None),
+                    getattr(props, "pci_device_id", None))
+            handles = amdsmi.amdsmi_get_processor_handles()
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)        # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if want[1] is None or (int(bus, 16) == want[1] and int(dom, 16) == want[0]):
+                    self.handle = h
+                    break
+            if self.handle is None and len(handles) == 1:
+                self.handle = handles[0]
+            if self.handle is None:
+                self.error = f"no amdsmi device matches PCI bus {want}"
+            else:
+                self.read()
+        except Exception as e:                                  # no amdsmi, no permission, ...
+            self.handle = None
+            self.error = repr(e)[:200]
+
+    def read(self):
+        """Mean current graphics clock over the XCDs in MHz (the gpu_metrics table), else the
+        clock_info reading."""
+        a = self.amdsmi
+        try:
+            m = a.amdsmi_get_gpu_metrics_info(self.handle)
+            clks = [int(c) for c in m.get("current_gfxclks", []) if isinstance(c, (int, float)) and 0 < c < 10000]
+            if clks:
+                return sum(clks) / len(clks)
+        except Exception:
+            pass
+        return float(a.amdsmi_get_clock_info(self.handle, a.AmdSmiClkType.GFX)["clk"])
+
+    def sampler(self):
+        return _ClockSampler(self)
+
+
+class _ClockSampler:
+    def __init__(self, clock):
+        self.clock = clock
+        self.samples = []
+        self.stop = False
+        self.thread = None
+
+    def __enter__(self):
+        import threading
+        if self.clock.handle is None:
+            return self
+
+        def run():
+            while not self.stop:
+                try:
+                    self.samples.append((time.perf_counter(), self.clock.read()))
+                except Exception:
+                    return
+                time.sleep(0.004)
+        self.thread = threading.Thread(target=run, daemon=True)
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop = True
+        if self.thread is not None:
+            self.thread.join()
+        return False
+
+    def summary(self, since):
+        if self.clock.handle is None:
+            return {"error": self.clock.error}
+        xs = [c for t, c in self.samples if t >= since] or [c for _, c in self.samples]
+        if not xs:
+            return {"error": "no sample"}
+        return {"mean": round(sum(xs) / len(xs), 1), "min": min(xs), "max": max(xs), "samples": len(xs),
+                "when": "second half of the warm-up (the GPU runs the same workload back to back)"}
+
+
+CLOCK = None
+
+
 def time_steps(fns, steps, warmup):
-    """Run fns round-robin: warmup untimed, then `steps` timed between synchronisations.
-    Returns (wall ms per step, per-call event durations in ms) -- events on the current stream,
-    which is the stream the library launches on."""
+    """Run fns round-robin: at least `warmup` calls and at least WARM_MS of GPU time untimed (the host
+    synchronises every few calls, so the elapsed time is GPU time), then `steps` timed calls between
+    synchronisations. Returns (wall ms per step, per-call event durations in ms, timing summary) --
+    events on the current stream, which is the stream the library launches on."""
     import torch
     n = len(fns)
-    for i in range(warmup):
-        fns[i % n]()
     torch.cuda.synchronize()
+    sampler = CLOCK.sampler() if CLOCK is not None else None
+    calls = 0
+    t0 = time.perf_counter()
+    with (sampler if sampler is not None else _NullCtx()):
+        while True:
+            fns[calls % n]()
+            calls += 1
+            if calls % 4 == 0 or calls >= warmup:
+                torch.cuda.synchronize()
+                elapsed = (time.perf_counter() - t0) * 1e3
+                if calls >= warmup and elapsed >= WARM_MS:
+                    break
+    warm_ms = (time.perf_counter() - t0) * 1e3
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t1 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
         fns[i % n]()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
+    wall = (time.perf_counter() - t1) * 1e3 / steps
     durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall, durs
+    info = {"timed_calls": steps, "mean_ms": statistics.mean(durs), "median_ms": statistics.median(durs),
+            "min_ms": min(durs), "max_ms": max(durs), "wall_ms_per_call": wall,
+            "warmup_calls": calls, "warmup_ms": round(warm_ms, 2)}
+    if sampler is not None:
+        info["gfx_clock_mhz"] = sampler.summary(t0 + warm_ms / 2e3)
+    return wall, durs, info
+
+
+class _NullCtx:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
 
 
 def to_device(case, dev):
@@ -125,7 +246,7 @@ def decode_section(lib, case, splits, steps, warmup, label, rotate=True):
     hkv, bs = case.num_kv_heads, case.block_size
     maxblk = case.block_table.shape[1]
     s = lib.attn_decode_num_splits(b, hkv, d, 0 if case.kv_format == "bf16" else 1, bs, maxblk, splits)
-    ws = torch.empty(max(1, lib.attn_decode_workspace_bytes(b, hkv, d, s)), dtype=torch.uint8, device=case.q.device)
+    ws = torch.empty(max(1, lib.attn_decode_workspace_bytes(b, hq, d, s)), dtype=torch.uint8, device=case.q.device)
     out = torch.empty_like(case.q)
     lse = torch.empty((b, hq), dtype=torch.float32, device=case.q.device)
 
@@ -133,12 +254,13 @@ def decode_section(lib, case, splits, steps, warmup, label, rotate=True):
         return lambda: lib.attn_decode_paged(case.q, kc, vc, case.block_table, case.seq_lens_k, case.scale,
                                              k_scale=case.k_scale, v_scale=case.v_scale, out=out, lse=lse,
                                              num_splits=s, workspace=ws)
-    wall, durs = time_steps([make(kc, vc) for kc, vc in caches], steps, warmup)
+    wall, durs, info = time_steps([make(kc, vc) for kc, vc in caches], steps, warmup)
     kern = statistics.mean(durs)
     log(f"[bench] {label}: partitions={s} copies={copies} wall/step={wall:.4f} ms call mean={kern:.4f} "
         f"median={statistics.median(durs):.4f} min={min(durs):.4f} ms -> {kv_bytes / kern / 1e6:.1f} GB/s")
     return {"kv_bytes": kv_bytes, "splits": s, "wall_ms": wall, "kernel_ms_mean": kern,
-            "kernel_ms_median": statistics.median(durs), "kernel_ms_min": min(durs), "out": out, "lse": lse}
+            "kernel_ms_median": statistics.median(durs), "kernel_ms_min": min(durs), "out": out, "lse": lse,
+            "timing": info}
 
 
 def prefill_section(lib, case, steps, warmup, window=0):
@@ -150,12 +272,12 @@ def prefill_section(lib, case, steps, warmup, window=0):
     def call():
         lib.attn_prefill_varlen(case.q, case.k, case.v, case.cu_seqlens, case.causal, case.scale, out=out,
                                 lse=lse, max_seqlen=case.max_seqlen, window=window)
-    wall, durs = time_steps([call], steps, warmup)
+    wall, durs, info = time_steps([call], steps, warmup)
     kern = statistics.mean(durs)
     log(f"[bench] prefill{f' window={window}' if window else ''}: wall/step={wall:.4f} ms kernel mean={kern:.4f} "
         f"min={min(durs):.4f} ms -> {flops / kern / 1e9:.1f} TFLOP/s")
     return {"flops": flops, "wall_ms": wall, "kernel_ms_mean": kern, "kernel_ms_min": min(durs), "out": out,
-            "lse": lse}
+            "lse": lse, "timing": info}
 
 
 def prefill_fp8_section(lib, case, steps, warmup):
@@ -168,12 +290,12 @@ def prefill_fp8_section(lib, case, steps, warmup):
     def call():
         lib.attn_prefill_varlen_fp8(case.q, case.k, case.v, case.q_scale, case.k_scale, case.v_scale,
                                     case.cu_seqlens, case.causal, case.scale, out=out, lse=lse, max_seqlen=mx)
-    wall, durs = time_steps([call], steps, warmup)
+    wall, durs, info = time_steps([call], steps, warmup)
     kern = statistics.mean(durs)
     log(f"[bench] prefill fp8: wall/step={wall:.4f} ms kernel mean={kern:.4f} min={min(durs):.4f} ms -> "
         f"{flops / kern / 1e9:.1f} TFLOP/s")
     return {"flops": flops, "wall_ms": wall, "kernel_ms_mean": kern, "kernel_ms_min": min(durs), "out": out,
-            "lse": lse}
+            "lse": lse, "timing": info}
 
 
 def mixed_section(lib, case, steps, warmup):
@@ -187,7 +309,7 @@ def mixed_section(lib, case, steps, warmup):
     b = case.seq_lens_k.numel()
     s = lib.attn_decode_num_splits(b, case.num_kv_heads, case.head_dim, 1, case.block_size,
                                    case.block_table.shape[1], 0)
-    ws = torch.empty(lib.attn_varlen_workspace_bytes(b, case.num_kv_heads, case.head_dim, s), dtype=torch.uint8,
+    ws = torch.empty(lib.attn_varlen_workspace_bytes(b, case.num_q_heads, case.head_dim, s), dtype=torch.uint8,
                      device=case.q.device)
     out = torch.empty_like(case.q)
     lse = torch.empty((case.q.shape[0], case.q.shape[1]), dtype=torch.float32, device=case.q.device)
@@ -197,13 +319,13 @@ def mixed_section(lib, case, steps, warmup):
         lib.attn_varlen_paged(case.q, case.k_cache, case.v_cache, case.block_table, case.cu_seqlens_q,
                               case.seq_lens_k, True, case.scale, k_scale=case.k_scale, v_scale=case.v_scale,
                               out=out, lse=lse, max_q_len=max_q, num_splits=s, workspace=ws)
-    wall, durs = time_steps([call], steps, warmup)
+    wall, durs, info = time_steps([call], steps, warmup)
     kern = statistics.mean(durs)
     t_star = max(flops / (MFMA_BF16_PEAK_TFS * 1e9), (dec_bytes + pre_kv_bytes) / (HBM_PEAK_GBS * 1e6))
     log(f"[bench] mixed c5: call mean={kern:.4f} ms -> prefill part {flops / kern / 1e9:.1f} TFLOP/s, decode part "
         f"{dec_bytes / kern / 1e6:.1f} GB/s; roofline lower bound {t_star:.4f} ms ({t_star / kern:.3f})")
     return {"flops": flops, "decode_kv_bytes": dec_bytes, "prefill_kv_bytes": pre_kv_bytes, "ms": kern,
-            "wall_ms": wall, "t_star_ms": t_star, "out": out, "lse": lse}
+            "wall_ms": wall, "t_star_ms": t_star, "out": out, "lse": lse, "timing": info}
 
 
 def multi_token_section(lib, case, steps, warmup, q_len=4):
@@ -219,19 +341,19 @@ def multi_token_section(lib, case, steps, warmup, q_len=4):
     cu = torch.arange(0, b * q_len + 1, q_len, dtype=torch.int32, device=dev)
     kv_bytes = workmodel.kv_bytes(case.kv_lens, case.num_kv_heads, d, 2)
     s = lib.attn_decode_num_splits(b, case.num_kv_heads, d, 0, case.block_size, case.block_table.shape[1], 0)
-    ws = torch.empty(lib.attn_varlen_workspace_bytes(b, case.num_kv_heads, d, s), dtype=torch.uint8, device=dev)
+    ws = torch.empty(lib.attn_varlen_workspace_bytes(b, hq, d, s), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
 
     def call():
         lib.attn_varlen_paged(q, case.k_cache, case.v_cache, case.block_table, cu, case.seq_lens_k, True, case.scale,
                               out=out, max_q_len=q_len, num_splits=s, workspace=ws)
-    wall, durs = time_steps([call], steps, warmup)
+    wall, durs, info = time_steps([call], steps, warmup)
     kern = statistics.mean(durs)
     gbs = kv_bytes / kern / 1e6
     log(f"[bench] multi-token decode q_len={q_len}: call mean={kern * 1e3:.1f} us -> {gbs:.0f} GB/s")
     return {"workload": f"batch-32 paged decode cache (32/8 heads, D 128, bf16, 16-token pages), {q_len} new "
                         f"query rows per request (g * q_len = 16 rows per KV head)",
-            "q_len": q_len, "kv_bytes": kv_bytes, "ms": kern, "wall_ms": wall, "gbs": gbs,
+            "q_len": q_len, "kv_bytes": kv_bytes, "ms": kern, "wall_ms": wall, "gbs": gbs, "timing": info,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
 
@@ -257,7 +379,7 @@ def append_section(lib, steps, warmup):
     def call():
         lib.attn_kv_append_paged(t["k_new"], t["v_new"], kc, vc, t["block_table"], t["cu_seqlens_new"],
                                  t["seq_lens_k"], k_scale=t["k_scale"], v_scale=t["v_scale"])
-    wall, durs = time_steps([call], steps, warmup)
+    wall, durs, info = time_steps([call], steps, warmup)
     kern = statistics.mean(durs)
     tn = sum(new)
     nbytes = tn * 4 * 256 * 2 * 2 + tn * 4 * 256 * 1 * 2
@@ -265,7 +387,7 @@ def append_section(lib, steps, warmup):
     log(f"[bench] append c5 geometry: {tn} tokens, call mean={kern * 1e3:.1f} us -> {gbs:.0f} GB/s")
     return {"workload": "KV-cache append of a mixed step: 8 x 2048 + 120 x 1 new tokens, 4 KV heads, D 256, "
                         "bf16 in, fp8 e4m3fn out (per-head scales), 16-token pages",
-            "tokens": tn, "bytes": nbytes, "ms": kern, "wall_ms": wall, "gbs": gbs,
+            "tokens": tn, "bytes": nbytes, "ms": kern, "wall_ms": wall, "gbs": gbs, "timing": info,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
                          "traffic": measured_traffic("append_c5", ["append.hip"])}}
@@ -321,13 +443,14 @@ def cpu_baseline_decode(case):
             case.cu_seqlens_q.cpu().numpy(), case.seq_lens_k.cpu().numpy(), True, case.scale)
     b, hq, d = case.q.shape
     units = [(i, h) for i in range(b) for h in range(hq)]
-    workers = min(16, os.cpu_count() or 1)
+    workers = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     _, _, wall, used = parallel.run_units("paged", args, {"kv_format": "bf16"}, units,
                                           case.cu_seqlens_q.cpu().numpy(), (b, hq, d), (b, hq), workers=workers)
     kv = workmodel.kv_bytes(case.kv_lens, case.num_kv_heads, case.head_dim, 2)
     return {"value": kv / wall / 1e9, "unit": "GB/s", "cores": used, "kind": "oracle",
             "sample": f"the whole decode batch ({b} requests x {hq} heads, {kv / 1e6:.0f} MB of KV), "
-                      f"fp64 numpy, one BLAS thread per worker process; wall {wall:.2f} s"}
+                      f"fp64 numpy, one worker process with one BLAS thread per host core the process may run "
+                      f"on ({workers} of os.cpu_count() = {os.cpu_count()}); wall {wall:.2f} s"}
 
 
 def main():
@@ -344,6 +467,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] device: {torch.cuda.get_device_name(dev)}; library {lib.library_path()}")
+    global CLOCK
+    CLOCK = GpuClock(0)
+    log(f"[bench] clock readings: {'amdsmi' if CLOCK.handle is not None else CLOCK.error}")
     run = (lambda name: a.only is None or a.only == name)
     extra = {}
 
@@ -362,6 +488,7 @@ def main():
             par = sampled_parity_paged(c2_host, dec["out"], dec["lse"], units)
             log(f"[bench] decode c2 parity on {par['units']} sampled (request, head) units: {par}")
             extra["decode_parity_sample"] = par
+        extra["decode_c2_timing"] = dec["timing"]
         extra["multi_token_decode"] = multi_token_section(lib, c2, a.steps, a.warmup)
         del c2
         torch.cuda.empty_cache()
@@ -380,11 +507,11 @@ def main():
 
     if run("c3"):
         c3 = synth.config_case("c3", device=dev)
-        pre = prefill_section(lib, c3, max(10, a.steps // 2), max(2, a.warmup // 20))
+        pre = prefill_section(lib, c3, max(10, a.steps // 2), a.warmup)
         tf = pre["flops"] / pre["kernel_ms_mean"] / 1e9
         extra["prefill_c3"] = {
             "workload": "causal varlen prefill, 4 x 8192 tokens, 32/8 heads, D 128, bf16, out + LSE",
-            "tflops": tf, "ms": pre["kernel_ms_mean"], "wall_ms": pre["wall_ms"],
+            "tflops": tf, "ms": pre["kernel_ms_mean"], "wall_ms": pre["wall_ms"], "timing": pre["timing"],
             "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tf / MFMA_BF16_PEAK_TFS,
                          "traffic": measured_traffic("prefill_c3", ["common.h", "prefill_core.h", "prefill_pp.h", "prefill.hip"])},
@@ -394,12 +521,12 @@ def main():
             par = sampled_parity_prefill(c3, pre["out"], pre["lse"], units)
             log(f"[bench] prefill parity on {units}: {par}")
             extra["prefill_c3"]["parity_sample"] = par
-        pw = prefill_section(lib, c3, max(10, a.steps // 2), max(2, a.warmup // 20), window=4096)
+        pw = prefill_section(lib, c3, max(10, a.steps // 2), a.warmup, window=4096)
         tfw = pw["flops"] / pw["kernel_ms_mean"] / 1e9
         extra["prefill_c3_window4096"] = {
             "workload": "the same causal prefill with a 4096-key sliding window (algorithmic FLOPs over the "
                         "windowed visible pairs)",
-            "tflops": tfw, "ms": pw["kernel_ms_mean"], "algorithmic_flops": pw["flops"],
+            "tflops": tfw, "ms": pw["kernel_ms_mean"], "algorithmic_flops": pw["flops"], "timing": pw["timing"],
             "roofline": {"bound": "mfma", "achieved": tfw, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tfw / MFMA_BF16_PEAK_TFS, "traffic": None}}
         del c3, pre, pw
@@ -407,12 +534,13 @@ def main():
 
     if run("c3fp8"):
         c3f = synth.make_prefill_fp8(3, [8192] * 4, 32, 8, 128, device=dev)
-        pf = prefill_fp8_section(lib, c3f, max(10, a.steps // 2), max(2, a.warmup // 20))
+        pf = prefill_fp8_section(lib, c3f, max(10, a.steps // 2), a.warmup)
         tf8 = pf["flops"] / pf["kernel_ms_mean"] / 1e9
         extra["prefill_c3_fp8"] = {
             "workload": "the same causal prefill with e4m3fn Q/K/V and per-head scales (N(0,1) draws, scale = "
                         "amax/448 per head), fp8 MFMA, P rounded to e4m3, out bf16 + LSE",
             "tflops": tf8, "ms": pf["kernel_ms_mean"], "wall_ms": pf["wall_ms"], "algorithmic_flops": pf["flops"],
+            "timing": pf["timing"],
             "roofline": {"bound": "mfma", "achieved": tf8, "peak": MFMA_FP8_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tf8 / MFMA_FP8_PEAK_TFS,
                          "traffic": measured_traffic("prefill_c3_fp8", ["common.h", "prefill_core.h", "prefill_pp.h",
@@ -435,7 +563,7 @@ def main():
         gbs = best["kv_bytes"] / best["kernel_ms_mean"] / 1e6
         extra["decode_c4"] = {
             "workload": "split-KV decode, 2 x 131072 tokens, 32/2 heads, D 128, bf16 KV, 64-token blocks",
-            "gbs": gbs, "partitions": best["splits"], "ms": best["kernel_ms_mean"],
+            "gbs": gbs, "partitions": best["splits"], "ms": best["kernel_ms_mean"], "timing": best["timing"],
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
                          "traffic": measured_traffic("decode_c4", ["common.h", "decode_core.h", "decode.hip"])}}
@@ -452,11 +580,11 @@ def main():
         c5 = synth.config_case("c5", device=dev)
         log(f"[bench] mixed workload ready in {time.perf_counter() - t:.1f} s: q rows {c5.q.shape[0]}, "
             f"keys {sum(c5.kv_lens)}")
-        mx = mixed_section(lib, c5, max(5, a.steps // 5), max(2, a.warmup // 50))
+        mx = mixed_section(lib, c5, max(5, a.steps // 5), a.warmup)
         extra["mixed_c5"] = {
             "workload": "one call: 8 prefill chunks of 2048 over cached prefixes U[0, 32768] + 120 decodes with "
                         "contexts U[512, 32768], 16/4 heads, D 256, fp8 e4m3fn KV with per-head scales",
-            "ms": mx["ms"], "prefill_tflops": mx["flops"] / mx["ms"] / 1e9,
+            "ms": mx["ms"], "timing": mx["timing"], "prefill_tflops": mx["flops"] / mx["ms"] / 1e9,
             "decode_gbs": mx["decode_kv_bytes"] / mx["ms"] / 1e6,
             "algorithmic_flops": mx["flops"], "decode_kv_bytes": mx["decode_kv_bytes"],
             "prefill_kv_bytes": mx["prefill_kv_bytes"],

@@ -34,6 +34,14 @@
  *       request b lives in physical block block_table[b][i]; token t is slot
  *       t % block_size of logical block t / block_size ("Optimization 1",
  *       section 3.4 PagedAttention; "Attention kernels", section "Paged KV and kernels").
+ *   - The V page departs from the K page order ([block_size, head_dim]): it is
+ *     stored transposed. The kernels multiply P by V on the matrix cores with the
+ *     keys as the reduction axis; with tokens innermost each lane's operand (8
+ *     consecutive keys of one head_dim row) is one contiguous 16-byte load
+ *     straight from the page, with no transpose through LDS. A page has the same
+ *     byte count either way. When block_size == head_dim the two orders have the
+ *     same shape, so nothing can detect a V cache written in the K order: the
+ *     attention is then silently wrong. The append call writes this order.
  *   - head_dim must be 128 or 256; num_q_heads must be a multiple of
  *     num_kv_heads; block_size must be 16, 32, 64, 128 or 256; paged calls
  *     take at most 16384 requests.
@@ -47,7 +55,12 @@
  *   - stream is a hipStream_t (NULL = the default stream). Calls return once
  *     the work is enqueued; results are valid after the stream synchronises.
  *   - Argument validation is synchronous and happens before anything is
- *     launched; on any error nothing is launched and nothing is written.
+ *     launched: a validation error (ATTN_ERR_NULL, _SHAPE, _UNSUPPORTED,
+ *     _WORKSPACE) launches nothing and writes nothing. ATTN_ERR_LAUNCH means the
+ *     HIP runtime refused one of the call's kernels; kernels of the call
+ *     enqueued before it may then have run, so out / lse / the workspace (or the
+ *     caches, for the append) are undefined. An error left pending by earlier,
+ *     unrelated HIP work is neither reported as this call's nor cleared.
  *     Device-resident values (cu_seqlens, seq_lens, block-table entries) are
  *     NOT validated: they are the caller's contract (monotone cu_seqlens,
  *     0 <= seq_lens[b] <= max_blocks_per_seq * block_size, table entries in
@@ -89,16 +102,17 @@ const char* attn_status_string(attn_status status);
  *   out [total_tokens, num_q_heads, head_dim] bf16 (round to nearest even)
  *   lse [total_tokens, num_q_heads] fp32, or NULL to skip it
  *   max_seqlen: an upper bound on every request's length (sizes the grid)
+ *   window: sliding window (0 = none), see the conventions above
  * Needs no workspace: nothing but out and lse is written. Sizes are checked
  * first; total_tokens = 0 (or max_seqlen = 0) is then a no-op that returns
  * ATTN_OK whatever the pointers (empty tensors may pass NULL).
  */
 attn_status attn_prefill_varlen(const void* q, const void* k, const void* v,
-                                const int32_t* cu_seqlens, int32_t causal, float scale, int32_t window,
+                                const int32_t* cu_seqlens, int32_t causal, float scale,
                                 void* out, float* lse,
                                 int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                void* stream);
+                                int32_t window, void* stream);
 
 /*
  * FP8 varlen prefill ("Attention kernels", section "FlashAttention": the third
@@ -122,10 +136,10 @@ attn_status attn_prefill_varlen(const void* q, const void* k, const void* v,
  */
 attn_status attn_prefill_varlen_fp8(const void* q, const void* k, const void* v, const float* q_scale,
                                     const float* k_scale, const float* v_scale, const int32_t* cu_seqlens,
-                                    int32_t causal, float scale, int32_t window, void* out, float* lse,
+                                    int32_t causal, float scale, void* out, float* lse,
                                     int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                    void* stream);
+                                    int32_t window, void* stream);
 
 /*
  * Number of partitions (partition workgroups) a paged decode call will use
@@ -146,10 +160,13 @@ int32_t attn_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t h
  * Workspace bytes a paged decode / varlen-paged call needs for num_splits
  * (resolved, >= 1) partitions: two partial results per partition (16 rows x
  * head_dim fp32 outputs plus 16 fp32 LSEs each) and num_seqs + 1 int32 chunk
- * offsets. The contents need no initialisation; calls that share one
- * workspace must not overlap in time (enqueue them on one stream).
+ * offsets. The size does not depend on the head count (a partition holds at
+ * most 16 rows of one KV group); num_q_heads must only be positive. Returns 0
+ * for a non-positive argument. The contents need no initialisation; calls
+ * that share one workspace must not overlap in time (enqueue them on one
+ * stream).
  */
-size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t num_splits);
 
 /*
@@ -167,6 +184,8 @@ size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32
  *   out [num_seqs, num_q_heads, head_dim] bf16; lse [num_seqs, num_q_heads] fp32 or NULL
  *   num_splits: 0 = automatic (attn_decode_num_splits), else the partition count
  *   workspace: device scratch of >= attn_decode_workspace_bytes(...) bytes.
+ *   kv_dtype, k_scale, v_scale, window: as above (they follow the arguments of
+ *   the plain bf16 call, so a bf16 caller passes ATTN_KV_BF16, NULL, NULL, 0).
  * A (request, kv head) whose keys lie in one partition's share is written by
  * that partition; otherwise each partition writes a normalised partial output
  * and its LSE to the workspace, and a second kernel, enqueued on the same
@@ -174,13 +193,13 @@ size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32
  * Requires num_q_heads / num_kv_heads <= 16.
  */
 attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                              int32_t kv_dtype, const float* k_scale, const float* v_scale,
-                              const int32_t* block_table, const int32_t* seq_lens, float scale, int32_t window,
-                              void* out, float* lse,
+                              const int32_t* block_table, const int32_t* seq_lens, float scale, void* out,
                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                              int32_t max_blocks_per_seq, int32_t num_splits,
-                              void* workspace, size_t workspace_bytes, void* stream);
+                              int32_t max_blocks_per_seq, int32_t num_splits, float* lse,
+                              void* workspace, size_t workspace_bytes,
+                              int32_t kv_dtype, const float* k_scale, const float* v_scale, int32_t window,
+                              void* stream);
 
 /*
  * Mixed varlen batch over a paged cache in one attention launch ("Attention
@@ -197,19 +216,19 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
  * With head_dim 256, num_seqs above 5627 returns ATTN_ERR_UNSUPPORTED (the
  * kernel keeps per-request offsets in LDS beside its 138 KB of tiles).
  */
-size_t attn_varlen_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+size_t attn_varlen_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t num_splits);
 
 attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_cache,
                               int32_t kv_dtype, const float* k_scale, const float* v_scale,
                               const int32_t* block_table, const int32_t* cu_seqlens_q,
-                              const int32_t* seq_lens_k, int32_t causal, float scale, int32_t window,
+                              const int32_t* seq_lens_k, int32_t causal, float scale,
                               void* out, float* lse,
                               int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                               int32_t num_splits, void* workspace, size_t workspace_bytes,
-                              void* stream);
+                              int32_t window, void* stream);
 
 /*
  * Append new tokens' K and V to a paged cache, the step before attention in

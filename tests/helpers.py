@@ -8,10 +8,11 @@ import oracle
 MAX_ABS = 1e-2      # bf16 outputs vs the fp64 oracle
 MEAN_ABS = 1e-3
 LSE_ABS = 1e-3
-MAX_ABS_FP8 = 3e-2  # the fp8-KV workload, and fp8 prefill
-# fp8 prefill rounds P to e4m3 (relative RMS error 2^-4 / sqrt(3) ~ 0.036 per weight) on tiles
-# that mask no key; over a row's >= 64 unmasked keys that averages to about 0.036 E|v| / 8 ~ 4e-3
-MEAN_ABS_FP8 = 5e-3
+# fp8 prefill rounds P to e4m3 (the kernel's approximation, not part of the definition): max-abs
+# 3e-2 is the fp8 bar; the mean-abs bar stays the bf16 one (1e-3). The fp8-KV attention calls
+# consume the same codes as the oracle, so they are held to the bf16 bars.
+MAX_ABS_FP8 = 3e-2
+MEAN_ABS_FP8 = 1e-3
 
 
 def bf16_np(t):

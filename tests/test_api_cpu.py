@@ -38,9 +38,9 @@ def _prefill(**kw):
                 total=16, maxlen=16, hq=4, hkv=1, d=128)
     args.update(kw)
     return _lib.load().attn_prefill_varlen(args["q"], args["k"], args["v"], args["cu"], args["causal"],
-                                           args["scale"], args["window"], args["out"], args["lse"], args["nseq"],
-                                           args["total"],
-                                           args["maxlen"], args["hq"], args["hkv"], args["d"], None)
+                                           args["scale"], args["out"], args["lse"], args["nseq"], args["total"],
+                                           args["maxlen"], args["hq"], args["hkv"], args["d"], args["window"],
+                                           None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -62,9 +62,9 @@ def _prefill_fp8(**kw):
                 lse=None, nseq=1, total=16, maxlen=16, hq=4, hkv=1, d=128)
     args.update(kw)
     return _lib.load().attn_prefill_varlen_fp8(args["q"], args["k"], args["v"], args["qs"], args["ks"], args["vs"],
-                                               args["cu"], args["causal"], args["scale"], args["window"],
-                                               args["out"], args["lse"], args["nseq"], args["total"],
-                                               args["maxlen"], args["hq"], args["hkv"], args["d"], None)
+                                               args["cu"], args["causal"], args["scale"], args["out"], args["lse"],
+                                               args["nseq"], args["total"], args["maxlen"], args["hq"], args["hkv"],
+                                               args["d"], args["window"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -86,11 +86,10 @@ def _decode(**kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, kvt=0, ks=None, vs=None, table=FAKE, lens=FAKE, scale=0.1, window=0,
              out=FAKE, lse=None, nseq=2, hq=8, hkv=2, d=128, bs=16, nblk=10, maxblk=4, splits=1, ws=None, wsb=0)
     a.update(kw)
-    return _lib.load().attn_decode_paged(a["q"], a["kc"], a["vc"], a["kvt"], a["ks"], a["vs"], a["table"],
-                                         a["lens"], a["scale"], a["window"], a["out"], a["lse"], a["nseq"], a["hq"],
-                                         a["hkv"],
-                                         a["d"], a["bs"], a["nblk"], a["maxblk"], a["splits"], a["ws"], a["wsb"],
-                                         None)
+    return _lib.load().attn_decode_paged(a["q"], a["kc"], a["vc"], a["table"], a["lens"], a["scale"], a["out"],
+                                         a["nseq"], a["hq"], a["hkv"], a["d"], a["bs"], a["nblk"], a["maxblk"],
+                                         a["splits"], a["lse"], a["ws"], a["wsb"], a["kvt"], a["ks"], a["vs"],
+                                         a["window"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -120,28 +119,31 @@ def test_split_planning_and_workspace_sizes():
     assert lib.attn_decode_workspace_bytes(2, 2, 128, 1) == 2 * 16 * 129 * 4 + 3 * 4
     assert lib.attn_decode_workspace_bytes(2, 2, 128, 64) == 64 * 2 * 16 * 129 * 4 + 3 * 4
     assert lib.attn_decode_workspace_bytes(2, 2, 128, 0) == 0
+    # (num_seqs, num_q_heads, head_dim, num_splits): the size does not depend on the head count
+    assert lib.attn_decode_workspace_bytes(2, 32, 128, 4) == lib.attn_decode_workspace_bytes(2, 1, 128, 4)
+    assert lib.attn_decode_workspace_bytes(2, 0, 128, 4) == 0
 
 
 def test_varlen_validation():
     lib = _lib.load()
-    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, None, FAKE, 1, 0.1, 0, FAKE, None,
-                               2, 10, 5, 8, 2, 128, 16, 10, 4, 1, None, 0, None)
+    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, None, FAKE, 1, 0.1, FAKE, None, 2,
+                               10, 5, 8, 2, 128, 16, 10, 4, 1, None, 0, 0, None)
     assert st == 1                                   # cu_seqlens_q missing
-    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, 0, FAKE, None,
-                               2, 10, 11, 8, 2, 128, 16, 10, 4, 1, None, 0, None)
+    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None, 2,
+                               10, 11, 8, 2, 128, 16, 10, 4, 1, None, 0, 0, None)
     assert st == 2                                   # max_q_len > total_q
-    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, -1, FAKE, None,
-                               2, 10, 5, 8, 2, 128, 16, 10, 4, 1, None, 0, None)
+    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None, 2,
+                               10, 5, 8, 2, 128, 16, 10, 4, 1, None, 0, -1, None)
     assert st == 2                                   # negative window
     # head_dim 256: the mixed kernel's LDS (138 KB of tiles + one int per request) caps num_seqs at 5627
-    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, 0, FAKE, None,
-                               5628, 6000, 5, 8, 2, 256, 16, 10, 4, 1, None, 0, None)
+    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None, 5628,
+                               6000, 5, 8, 2, 256, 16, 10, 4, 1, None, 0, 0, None)
     assert st == 3
-    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, 0, FAKE, None,
-                               5627, 6000, 5, 8, 2, 256, 16, 10, 4, 1, None, 0, None)
+    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None, 5627,
+                               6000, 5, 8, 2, 256, 16, 10, 4, 1, None, 0, 0, None)
     assert st == 4                                   # passes the cap, then no workspace
-    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, 0, FAKE, None,
-                               16384, 20000, 5, 8, 2, 128, 16, 10, 4, 1, None, 0, None)
+    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None, 16384,
+                               20000, 5, 8, 2, 128, 16, 10, 4, 1, None, 0, 0, None)
     assert st == 4                                   # head_dim 128: no cap below the request limit
 
 

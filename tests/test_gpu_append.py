@@ -41,7 +41,8 @@ def _check(case, gpu):
 
 
 @pytest.mark.parametrize("kv_format", ["bf16", "e4m3fn"])
-@pytest.mark.parametrize("d,bs,hkv", [(128, 16, 2), (256, 16, 4), (128, 64, 1), (256, 32, 2)])
+@pytest.mark.parametrize("d,bs,hkv", [(128, 16, 2), (256, 16, 4), (128, 64, 1), (256, 32, 2), (128, 256, 2),
+                                      (256, 256, 1)])
 def test_append_mixed_batch(gpu, kv_format, d, bs, hkv):
     # decode tokens, chunks crossing page boundaries, an empty request, a first fill
     prior = [0, 5, 16, 100, 7, 0, 31, 250]

@@ -49,7 +49,7 @@ def test_decode_in_graph(gpu):
     out = torch.empty_like(case.q)
     lse = torch.empty((b, hq), dtype=torch.float32, device=gpu)
     splits = lib.attn_decode_num_splits(b, case.num_kv_heads, d, 0, case.block_size, case.block_table.shape[1], 0)
-    ws = torch.empty(lib.attn_decode_workspace_bytes(b, case.num_kv_heads, d, splits), dtype=torch.uint8,
+    ws = torch.empty(lib.attn_decode_workspace_bytes(b, case.num_q_heads, d, splits), dtype=torch.uint8,
                      device=gpu)
 
     def call():
@@ -65,7 +65,7 @@ def test_mixed_in_graph(gpu):
     out = torch.empty_like(case.q)
     lse = torch.empty((t, hq), dtype=torch.float32, device=gpu)
     splits = lib.attn_decode_num_splits(b, case.num_kv_heads, d, 1, case.block_size, case.block_table.shape[1], 0)
-    ws = torch.empty(lib.attn_varlen_workspace_bytes(b, case.num_kv_heads, d, splits), dtype=torch.uint8,
+    ws = torch.empty(lib.attn_varlen_workspace_bytes(b, case.num_q_heads, d, splits), dtype=torch.uint8,
                      device=gpu)
     max_q = max(case.q_lens)
 

@@ -8,7 +8,7 @@ import torch
 
 import attention_gqa_flash_02_amd as lib
 import synth
-from helpers import compare, oracle_paged, oracle_prefill, MAX_ABS_FP8
+from helpers import compare, oracle_paged, oracle_prefill
 
 pytestmark = pytest.mark.gpu
 
@@ -103,19 +103,20 @@ def test_decode_workspace_reuse(gpu):
 
 
 @pytest.mark.parametrize("kv_format", ["bf16", "e4m3fn"])
-@pytest.mark.parametrize("d,bs", [(128, 16), (128, 64), (256, 16), (256, 64), (256, 128)])
+@pytest.mark.parametrize("d,bs", [(128, 16), (128, 64), (128, 256), (256, 16), (256, 64), (256, 128), (256, 256)])
 def test_decode_every_variant(gpu, kv_format, d, bs):
     """Every decode kernel instantiation: head_dim 128/256 x bf16/e4m3fn pages x page rows of at
-    most 32 tokens (nontemporal V loads per half) and longer ones (loads issued in pairs)."""
+    most 32 tokens (nontemporal V loads per half) and longer ones (loads issued in pairs), up to
+    the largest block size the library takes (256). The oracle reads the same fp8 codes, so fp8
+    pages are held to the bf16 bar."""
     lens = [1, 31, 64, 65, 200, 700, 1500]
     gen = torch.Generator().manual_seed(60 + d + bs)
     case = _to(synth.make_paged(60 + d + bs, lens, [1] * len(lens), 16, 4, d, bs, kv_format=kv_format,
                                 lengths_drawn=gen), gpu)
-    tol = MAX_ABS_FP8 if kv_format == "e4m3fn" else 1e-2
     for splits in (0, 1, 5):
         out, lse = _run_decode(case, splits)
         ref_o, ref_l = oracle_paged(case)
-        compare(out, lse, ref_o, ref_l, max_abs=tol, label=f"decode {kv_format} d={d} bs={bs} splits={splits}")
+        compare(out, lse, ref_o, ref_l, label=f"decode {kv_format} d={d} bs={bs} splits={splits}")
 
 
 @pytest.mark.parametrize("d,bs", [(256, 16), (128, 32), (128, 16)])
@@ -127,7 +128,7 @@ def test_decode_fp8(gpu, d, bs):
     for splits in (1, 4):
         out, lse = _run_decode(case, splits)
         ref_o, ref_l = oracle_paged(case)
-        compare(out, lse, ref_o, ref_l, max_abs=MAX_ABS_FP8, label=f"fp8 d={d} bs={bs} splits={splits}")
+        compare(out, lse, ref_o, ref_l, label=f"fp8 d={d} bs={bs} splits={splits}")
 
 
 @pytest.mark.parametrize("g", [1, 2, 4, 8, 16])
@@ -159,11 +160,11 @@ def test_varlen_c5_shrunk(gpu):
     case = _to(synth.config_case("c5", shrink=16), gpu)   # 1 chunk of 128 over a prefix + 7 decodes
     out, lse = _run_varlen(case)
     ref_o, ref_l = oracle_paged(case)
-    compare(out, lse, ref_o, ref_l, max_abs=MAX_ABS_FP8, label="c5/16")
+    compare(out, lse, ref_o, ref_l, label="c5/16")
 
 
 @pytest.mark.parametrize("kv_format", ["bf16", "e4m3fn"])
-@pytest.mark.parametrize("d,bs", [(128, 16), (256, 16), (128, 64), (256, 64)])
+@pytest.mark.parametrize("d,bs", [(128, 16), (256, 16), (128, 64), (256, 64), (128, 256), (256, 256)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_varlen_mixed(gpu, kv_format, d, bs, causal):
     # decode rows (q_len 1..4 with g = 4 stay on the decode path), prefill chunks over prefixes,
@@ -176,9 +177,7 @@ def test_varlen_mixed(gpu, kv_format, d, bs, causal):
     for splits in (0, 3):
         out, lse = _run_varlen(case, splits)
         ref_o, ref_l = oracle_paged(case)
-        tol = MAX_ABS_FP8 if kv_format == "e4m3fn" else 1e-2
-        compare(out, lse, ref_o, ref_l, max_abs=tol,
-                label=f"mixed {kv_format} d={d} bs={bs} causal={causal} splits={splits}")
+        compare(out, lse, ref_o, ref_l, label=f"mixed {kv_format} d={d} bs={bs} causal={causal} splits={splits}")
 
 
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2), (16, 1), (32, 2)])
