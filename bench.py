@@ -14,7 +14,7 @@ roofline, checks sampled
 outputs against the fp64 oracle, and times the oracle itself on the host cores
 (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c1|c2|c3|c3fp8|c4|c5|append]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c1|c2|c3|c3w|c3fp8|c4|c5|append]
                        [--no-cpu-baseline] [--quick]
 Prints one JSON line.
 """
@@ -50,7 +50,7 @@ def parse():
     # up for at least WARM_MS of GPU time (the clocks rise over the first 20-40 ms of load).
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--splits", type=int, default=0, help="decode partitions (0 = library choice)")
-    ap.add_argument("--only", choices=["c1", "c2", "c3", "c3fp8", "c4", "c5", "append"], default=None,
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c3w", "c3fp8", "c4", "c5", "append"], default=None,
                     help="time one workload only (for profiling); the JSON line still names c2's metric")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the parity samples")
@@ -119,17 +119,15 @@ class GpuClock:
             self.error = repr(e)[:200]
 
     def read(self):
-        """Mean current graphics clock over the XCDs in MHz (the gpu_metrics table), else the
-        clock_info reading."""
+        """Current graphics clock in MHz (amdsmi clock_info; the gpu_metrics table, which can lag
+        by tens of milliseconds, only if that fails)."""
         a = self.amdsmi
         try:
+            return float(a.amdsmi_get_clock_info(self.handle, a.AmdSmiClkType.GFX)["clk"])
+        except Exception:
             m = a.amdsmi_get_gpu_metrics_info(self.handle)
             clks = [int(c) for c in m.get("current_gfxclks", []) if isinstance(c, (int, float)) and 0 < c < 10000]
-            if clks:
-                return sum(clks) / len(clks)
-        except Exception:
-            pass
-        return float(a.amdsmi_get_clock_info(self.handle, a.AmdSmiClkType.GFX)["clk"])
+            return sum(clks) / len(clks)
 
     def sampler(self):
         return _ClockSampler(self)
@@ -505,8 +503,9 @@ def main():
             "prefill_us": pre1["kernel_ms_mean"] * 1e3, "decode_us": dec1["kernel_ms_mean"] * 1e3}
         del p1, d1, pre1, dec1
 
-    if run("c3"):
+    if run("c3") or run("c3w"):
         c3 = synth.config_case("c3", device=dev)
+    if run("c3"):
         pre = prefill_section(lib, c3, max(10, a.steps // 2), a.warmup)
         tf = pre["flops"] / pre["kernel_ms_mean"] / 1e9
         extra["prefill_c3"] = {
@@ -521,6 +520,8 @@ def main():
             par = sampled_parity_prefill(c3, pre["out"], pre["lse"], units)
             log(f"[bench] prefill parity on {units}: {par}")
             extra["prefill_c3"]["parity_sample"] = par
+        del pre
+    if run("c3w"):
         pw = prefill_section(lib, c3, max(10, a.steps // 2), a.warmup, window=4096)
         tfw = pw["flops"] / pw["kernel_ms_mean"] / 1e9
         extra["prefill_c3_window4096"] = {
@@ -529,7 +530,9 @@ def main():
             "tflops": tfw, "ms": pw["kernel_ms_mean"], "algorithmic_flops": pw["flops"], "timing": pw["timing"],
             "roofline": {"bound": "mfma", "achieved": tfw, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tfw / MFMA_BF16_PEAK_TFS, "traffic": None}}
-        del c3, pre, pw
+        del pw
+    if run("c3") or run("c3w"):
+        del c3
         torch.cuda.empty_cache()
 
     if run("c3fp8"):

@@ -78,4 +78,4 @@ def test_mixed_step_full(gpu):
     # prefill chunks: first, middle and last chunk; decodes: first, two in the middle, last
     units = [(0, 0), (n_pre // 2, 5), (n_pre - 1, 15), (n_pre, 3), (n_pre + 50, 9), (n_pre + 90, 14), (n - 1, 12)]
     ref_o, ref_l = oracle_paged(case, units=units)
-    compare(out, lse, ref_o, ref_l, label="mixed step full (7 units)")
+    compare(out, lse, ref_o, ref_l, beyond_rounding=True, label="mixed step full (7 units)")

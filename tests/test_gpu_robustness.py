@@ -74,7 +74,8 @@ def test_nan_poison_decode(gpu, kv_format, d, bs):
     for splits in (0, 1, 7):
         out, lse = _decode(case, splits)
         ref_o, ref_l = oracle_paged(case)
-        compare(out, lse, ref_o, ref_l, label=f"NaN poison decode {kv_format} d={d} bs={bs} splits={splits}")
+        compare(out, lse, ref_o, ref_l, beyond_rounding=kv_format == "e4m3fn",
+                label=f"NaN poison decode {kv_format} d={d} bs={bs} splits={splits}")
 
 
 @pytest.mark.parametrize("kv_format", ["bf16", "e4m3fn"])
@@ -92,7 +93,7 @@ def test_nan_poison_mixed(gpu, kv_format, d, bs, causal):
     for splits in (0, 3):
         out, lse = _varlen(case, splits)
         ref_o, ref_l = oracle_paged(case)
-        compare(out, lse, ref_o, ref_l,
+        compare(out, lse, ref_o, ref_l, beyond_rounding=kv_format == "e4m3fn",
                 label=f"NaN poison mixed {kv_format} d={d} bs={bs} causal={causal} splits={splits}")
 
 
@@ -148,7 +149,7 @@ def test_page_permutation_bitwise(gpu, kv_format, d, bs):
             assert torch.equal(o1, o2) and torch.equal(l1, l2), f"decode differs under permutation {seed}"
     out, lse = _varlen(base, 0)
     ref_o, ref_l = oracle_paged(base)
-    compare(out, lse, ref_o, ref_l, label=f"permutation base {kv_format} d={d}")
+    compare(out, lse, ref_o, ref_l, beyond_rounding=kv_format == "e4m3fn", label=f"permutation base {kv_format} d={d}")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -286,4 +287,5 @@ def test_fp8_every_code_paged_prefill(gpu, d, bs):
     out, lse = _varlen(case, 0)
     _check_codes(case, kc, vc, table, out, lse, 2, f"mixed (prefill path) d={d} bs={bs}")
     ref_o, ref_l = oracle_paged(case, units=[(b, h) for b in range(0, 254, 17) for h in (0, 7, 15)])
-    compare(out, lse, ref_o, ref_l, label=f"every code, prefill path d={d}")
+    # row 1 mixes two keys whose codes reach 448 (outputs up to 224, where a bf16 ulp is 1)
+    compare(out, lse, ref_o, ref_l, beyond_rounding=True, label=f"every code, prefill path d={d}")

@@ -70,7 +70,8 @@ def test_varlen_window(gpu, kv_format, window, causal):
                                          v_scale=case.v_scale, num_splits=splits, window=window)
         torch.cuda.synchronize()
         ref_o, ref_l = oracle_paged(case, window=window)
-        compare(out, lse, ref_o, ref_l, label=f"varlen {kv_format} window={window} causal={causal} splits={splits}")
+        compare(out, lse, ref_o, ref_l, beyond_rounding=kv_format == "e4m3fn",
+                label=f"varlen {kv_format} window={window} causal={causal} splits={splits}")
 
 
 def test_varlen_window_mixed_step_d256(gpu):
@@ -80,4 +81,4 @@ def test_varlen_window_mixed_step_d256(gpu):
                                      window=700)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_paged(case, window=700)
-    compare(out, lse, ref_o, ref_l, label="c5/16 window=700")
+    compare(out, lse, ref_o, ref_l, beyond_rounding=True, label="c5/16 window=700")
