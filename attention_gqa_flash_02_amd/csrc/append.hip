@@ -8,19 +8,27 @@
 // stores e4m3fn(x / scale[h]): the quotient in correctly rounded fp32, clamped to +-448, converted
 // with round-to-nearest-even.
 //
-// Work layout: a workgroup takes 32 consecutive new-token rows of one kv head. Their K and V rows
-// are loaded into registers first, while the rows' requests are found: a coarse sample of
-// cu_seqlens_new, then (for more than 255 requests) the window that holds the first row, and a
-// search in LDS. K rows are written 16 bytes per thread; V rows are staged in LDS and written
-// column-wise, consecutive lanes taking consecutive tokens so that each d row of a page is
-// written as one contiguous run.
+// Work layout: a workgroup takes 64 consecutive new-token rows of one kv head. Its threads first
+// load those rows' K and V (32 contiguous bytes per thread and item: these loads do not depend on
+// where the rows land, so they are in flight while the rows' requests are found: a coarse sample of
+// cu_seqlens_new, then, for more than 255 requests, the window that holds the first row, and a
+// search in LDS) and their cache slots. Then:
+//   * K: every row's K row is one contiguous byte range of its page ([bs][D]); each thread converts
+//     the 16 bf16 values of each of its items into one 16-byte fp8 store (or stores them as two
+//     16-byte bf16 pieces).
+//   * V: the rows go to LDS and are written column-wise, the page being [D][bs] (tokens innermost).
+//     A 16-slot chunk of a page whose 16 slots are all new rows of this workgroup (same request) is
+//     written whole: (chunk, head_dim pair) items, one 16-byte piece per d row (two for a bf16
+//     cache). Every other row (the first and last rows of a request, a decode token, a chunk cut by
+//     the workgroup boundary) is written element by element, so that no slot outside the new rows
+//     is touched.
 #include "launch.h"
 
 namespace attn {
 
 namespace {
 
-constexpr int kAppendRows = 32;
+constexpr int kAppendRows = 64;    // new-token rows per workgroup
 
 // largest b in [0, B) with cu[b] <= row (the request holding new-token row `row`)
 __device__ int request_of_row_global(const int32_t* cu, int B, int row) {
@@ -51,41 +59,43 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 template <int D, bool FP8>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   constexpr int ELT = FP8 ? 1 : 2;
-  constexpr int CPR = D / 8;                   // 16-byte chunks of a bf16 row
-  constexpr int OCH = D * ELT / 16;            // 16-byte output chunks of a cache row
-  constexpr int IPO = 16 / ELT / 8;            // 16-byte input chunks per output chunk (2 for fp8)
-  constexpr int KPT = kAppendRows * OCH / 256; // K output chunks per thread
-  constexpr int VPT = kAppendRows * CPR / 256; // V input chunks per thread
-  static_assert(kAppendRows * OCH % 256 == 0 && kAppendRows * CPR % 256 == 0, "whole chunks per thread");
+  constexpr int IPR = D / 16;                  // 32-byte source items (16 bf16 values) per row
+  constexpr int ITEMS = kAppendRows * IPR / 256;   // items per thread
+  constexpr int HD = D / 2;                    // head_dim pairs
+  constexpr int VS = D + 2;                    // LDS row stride of the staged V rows (bf16)
+  static_assert(kAppendRows * IPR % 256 == 0, "whole items per thread");
   __shared__ int s_cu[257];
-  __shared__ long long s_kdst[kAppendRows];   // byte offset of each row's K slot
-  __shared__ long long s_vdst[kAppendRows];   // element offset of each row's V column (d = 0)
-  __shared__ __align__(16) bf16 s_v[kAppendRows][D];
+  __shared__ int s_req[kAppendRows];           // request of each row
+  __shared__ int s_pos[kAppendRows];           // cache position of each row
+  __shared__ long long s_page[kAppendRows];    // (block, head) page index of each row
+  __shared__ int s_full[kAppendRows];          // first row of each whole 16-slot chunk
+  __shared__ int s_prow[kAppendRows];          // the rows outside whole chunks
+  __shared__ int s_cnt[2];
+  __shared__ __align__(16) bf16 s_v[kAppendRows * VS];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int h = blockIdx.y;
   const int row0 = blockIdx.x * kAppendRows;
   const int nrows = min(kAppendRows, p.total_new - row0);
   const int B = p.num_seqs;
+  const size_t row_stride = (size_t)p.Hkv * D;              // elements between consecutive new rows
 
-  // ---- the new K and V rows go into registers first: these loads do not depend on where the
-  // rows land, so they are in flight while the requests and cache slots are looked up
-  u32x4 kin[KPT][IPO], vin[VPT];
+  // ---- the rows' K and V into registers: item i = tid + 256 u is row i / IPR, values 16 (i % IPR) ..
+  const bf16* __restrict__ knew = p.k_new;
+  const bf16* __restrict__ vnew = p.v_new;
+  u32x4 kin[ITEMS][2], vin[ITEMS][2];
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int idx = tid + 256 * i, r = idx / OCH, ch = idx % OCH;
-    const bf16* src = p.k_new + ((size_t)(row0 + r) * p.Hkv + h) * D + IPO * 8 * ch;
+  for (int u = 0; u < ITEMS; ++u) {
+    const int i = tid + 256 * u, r = min(i / IPR, nrows - 1), c = i % IPR;
+    const size_t off = (size_t)(row0 + r) * row_stride + (size_t)h * D + 16 * c;
 #pragma unroll
-    for (int u = 0; u < IPO; ++u)
-      kin[i][u] = r < nrows ? *reinterpret_cast<const u32x4*>(src + 8 * u) : u32x4{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int idx = tid + 256 * i, r = idx / CPR, ch = idx % CPR;
-    const bf16* src = p.v_new + ((size_t)(row0 + r) * p.Hkv + h) * D + 8 * ch;
-    vin[i] = r < nrows ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+    for (int q = 0; q < 2; ++q) {
+      kin[u][q] = *reinterpret_cast<const u32x4*>(knew + off + 8 * q);
+      vin[u][q] = *reinterpret_cast<const u32x4*>(vnew + off + 8 * q);
+    }
   }
 
-  // ---- requests of the 32 rows: coarse sample, then the window holding the first row (one round
+  // ---- requests of the rows: coarse sample, then the window holding the first row (one round
   // when the whole cu_seqlens_new fits the sample)
   const int step = (B + 256) / 256;            // ceil((B + 1) / 256) requests per sample
   s_cu[tid] = p.cu_seqlens_new[min(tid * step, B)];
@@ -123,55 +133,117 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
     }
     const int pos = p.seq_lens_k[b] - (c1 - c0) + (row - c0);
     const int blk = p.block_table[(size_t)b * p.max_blocks + pos / p.bs];
-    const int slot = pos % p.bs;
-    s_kdst[tid] = (((long long)blk * p.Hkv + h) * p.bs + slot) * D * ELT;
-    s_vdst[tid] = ((long long)blk * p.Hkv + h) * D * p.bs + slot;
+    s_req[tid] = b;
+    s_pos[tid] = pos;
+    s_page[tid] = (long long)blk * p.Hkv + h;
   }
   // ---- V rows into LDS
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int idx = tid + 256 * i, r = idx / CPR, ch = idx % CPR;
-    *reinterpret_cast<u32x4*>(&s_v[r][8 * ch]) = vin[i];
+  for (int u = 0; u < ITEMS; ++u) {
+    const int i = tid + 256 * u, r = i / IPR, c = i % IPR;
+    bf16* dst = s_v + r * VS + 16 * c;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) *reinterpret_cast<uint32_t*>(dst + 8 * q + 2 * w) = vin[u][q][w];
   }
   __syncthreads();
+  // a row lies in a whole chunk when the 16 rows of its 16-slot chunk are all new rows of this
+  // workgroup and of its request (then their positions are consecutive and fill the chunk)
+  bool whole = false, whole_start = false;
+  if (tid < nrows) {
+    const int i0 = tid - (s_pos[tid] & 15);
+    whole = i0 >= 0 && i0 + 15 < nrows && s_req[i0] == s_req[tid] && s_req[i0 + 15] == s_req[tid];
+    whole_start = whole && i0 == tid;
+  }
+  // compact the whole-chunk starts and the other rows (the rows are held by wave 0)
+  const uint64_t mw = __builtin_amdgcn_ballot_w64(whole_start);
+  const uint64_t mp = __builtin_amdgcn_ballot_w64(tid < nrows && !whole);
+  if (tid == 0) {
+    s_cnt[0] = __builtin_popcountll(mw);
+    s_cnt[1] = __builtin_popcountll(mp);
+  }
+  if (whole_start)
+    s_full[__builtin_amdgcn_mbcnt_hi((uint32_t)(mw >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mw, 0))] = tid;
+  if (tid < nrows && !whole)
+    s_prow[__builtin_amdgcn_mbcnt_hi((uint32_t)(mp >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mp, 0))] = tid;
+  __syncthreads();
+  const int nfull = s_cnt[0];
+  const int npart = s_cnt[1];
 
-  // ---- K rows: 16 output bytes per thread per chunk
+  // ---- K: each item (16 values of one row) becomes one 16-byte fp8 piece or two bf16 pieces
   const float ks = FP8 ? p.k_scale[h] : 1.f;
-  char* kc = reinterpret_cast<char*>(p.k_cache);
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int idx = tid + 256 * i, r = idx / OCH, ch = idx % OCH;
+  for (int u = 0; u < ITEMS; ++u) {
+    const int i = tid + 256 * u, r = i / IPR, c = i % IPR;
     if (r >= nrows) continue;
-    char* dst = kc + s_kdst[r] + 16 * ch;
+    char* dst = reinterpret_cast<char*>(p.k_cache) +
+                (((size_t)s_page[r] * p.bs + (s_pos[r] & (p.bs - 1))) * D + 16 * c) * ELT;
     if constexpr (!FP8) {
-      *reinterpret_cast<u32x4*>(dst) = kin[i][0];
+      *reinterpret_cast<u32x4*>(dst) = kin[u][0];
+      *reinterpret_cast<u32x4*>(dst + 16) = kin[u][1];
     } else {
-      const u32x4 a = kin[i][0], c = kin[i][IPO - 1];
+      const u32x4 a = kin[u][0], e = kin[u][1];
       u32x4 o;
       o[0] = quant4(bf16_lo(a[0]), bf16_hi(a[0]), bf16_lo(a[1]), bf16_hi(a[1]), ks);
       o[1] = quant4(bf16_lo(a[2]), bf16_hi(a[2]), bf16_lo(a[3]), bf16_hi(a[3]), ks);
-      o[2] = quant4(bf16_lo(c[0]), bf16_hi(c[0]), bf16_lo(c[1]), bf16_hi(c[1]), ks);
-      o[3] = quant4(bf16_lo(c[2]), bf16_hi(c[2]), bf16_lo(c[3]), bf16_hi(c[3]), ks);
+      o[2] = quant4(bf16_lo(e[0]), bf16_hi(e[0]), bf16_lo(e[1]), bf16_hi(e[1]), ks);
+      o[3] = quant4(bf16_lo(e[2]), bf16_hi(e[2]), bf16_lo(e[3]), bf16_hi(e[3]), ks);
       *reinterpret_cast<u32x4*>(dst) = o;
     }
   }
 
-  // ---- V columns: lane r % 32 takes token r, so a d row's tokens are written side by side
+  // ---- V, whole chunks: (chunk, head_dim pair) items
   const float vs = FP8 ? p.v_scale[h] : 1.f;
-  const int r = tid % kAppendRows;
-  if (r < nrows) {
-    const long long vdst = s_vdst[r];
-    for (int d = tid / kAppendRows; d < D; d += 256 / kAppendRows) {
-      const bf16 x = s_v[r][d];
-      if constexpr (!FP8) {
-        reinterpret_cast<bf16*>(p.v_cache)[vdst + (long long)d * p.bs] = x;
-      } else {
-        const float q = fminf(fmaxf((float)x / vs, -448.f), 448.f);
-        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false);
-        reinterpret_cast<uint8_t*>(p.v_cache)[vdst + (long long)d * p.bs] = (uint8_t)(w & 0xff);
+  for (int it = tid; it < nfull * HD; it += 256) {
+    const int i0 = s_full[it / HD], d = 2 * (it % HD);
+    uint32_t w[16];                                           // bf16 pairs (d, d + 1) of the 16 rows
+#pragma unroll
+    for (int t = 0; t < 16; ++t) w[t] = *reinterpret_cast<const uint32_t*>(s_v + (i0 + t) * VS + d);
+    const size_t e0 = ((size_t)s_page[i0] * D + d) * p.bs + (s_pos[i0] & (p.bs - 1));   // (d, first slot)
+    if constexpr (!FP8) {
+      bf16* v0 = reinterpret_cast<bf16*>(p.v_cache) + e0;
+      bf16* v1 = v0 + p.bs;                                   // the d + 1 row
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        u32x4 lo4, hi4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t x0 = w[8 * q + 2 * c], x1 = w[8 * q + 2 * c + 1];
+          lo4[c] = (x0 & 0xffffu) | (x1 << 16);               // d row: slots 2c, 2c + 1
+          hi4[c] = (x0 >> 16) | (x1 & 0xffff0000u);           // d + 1 row
+        }
+        *reinterpret_cast<u32x4*>(v0 + 8 * q) = lo4;
+        *reinterpret_cast<u32x4*>(v1 + 8 * q) = hi4;
       }
+    } else {
+      uint8_t* v0 = reinterpret_cast<uint8_t*>(p.v_cache) + e0;
+      uint32_t q0[4], q1[4];                                  // codes of the d and d + 1 rows
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        q0[c] = quant4(bf16_lo(w[4 * c]), bf16_lo(w[4 * c + 1]), bf16_lo(w[4 * c + 2]), bf16_lo(w[4 * c + 3]), vs);
+        q1[c] = quant4(bf16_hi(w[4 * c]), bf16_hi(w[4 * c + 1]), bf16_hi(w[4 * c + 2]), bf16_hi(w[4 * c + 3]), vs);
+      }
+      *reinterpret_cast<u32x4*>(v0) = u32x4{q0[0], q0[1], q0[2], q0[3]};
+      *reinterpret_cast<u32x4*>(v0 + p.bs) = u32x4{q1[0], q1[1], q1[2], q1[3]};
     }
   }
+
+  // ---- V, the other rows: (row, head_dim pair) items
+  for (int it = tid; it < npart * HD; it += 256) {
+    const int r = s_prow[it / HD], d = 2 * (it % HD);
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(s_v + r * VS + d);
+    const size_t e0 = ((size_t)s_page[r] * D + d) * p.bs + (s_pos[r] & (p.bs - 1));
+    if constexpr (!FP8) {
+      reinterpret_cast<uint16_t*>(p.v_cache)[e0] = (uint16_t)(w & 0xffffu);
+      reinterpret_cast<uint16_t*>(p.v_cache)[e0 + p.bs] = (uint16_t)(w >> 16);
+    } else {
+      const uint32_t q = quant4(bf16_lo(w), bf16_hi(w), 0.f, 0.f, vs);
+      reinterpret_cast<uint8_t*>(p.v_cache)[e0] = (uint8_t)(q & 0xffu);
+      reinterpret_cast<uint8_t*>(p.v_cache)[e0 + p.bs] = (uint8_t)((q >> 8) & 0xffu);
+    }
+  }
+  (void)lane;
 }
 
 template <int D, bool FP8>

@@ -15,11 +15,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(PagedParams p) {
   merge_row<D, CH>(p, blockIdx.z, blockIdx.y, blockIdx.x, reinterpret_cast<float*>(smem_raw));
 }
 
-// Dynamic LDS of the partition kernel: 128 floats of statistics and four waves' O rows, then the
-// chunk prefix sums (num_seqs + 1) and 4 scratch ints.
+// Dynamic LDS of the partition kernel (4 waves): the statistics and the waves' O rows, then the
+// chunk prefix sums (num_seqs + 1) and one scratch int per wave.
 template <int D>
 static size_t decode_lds_bytes(int rows_max, int num_seqs) {
-  return (size_t)(128 + 4 * rows_max * D) * sizeof(float) + ((size_t)num_seqs + 5) * sizeof(int);
+  return (size_t)decode_combine_floats<D, 4>(rows_max) * sizeof(float) + ((size_t)num_seqs + 5) * sizeof(int);
 }
 
 template <int D>
@@ -57,7 +57,7 @@ template <int D, int KVT, int NU, bool LONGV>
 static hipError_t launch_decode_t(const PagedParams& p, int rows_max, hipStream_t stream) {
   hipError_t e = ensure_decode_attrs<D, KVT, NU, LONGV>();
   if (e != hipSuccess) return e;
-  const int combine_floats = 128 + 4 * rows_max * D;
+  const int combine_floats = decode_combine_floats<D, 4>(rows_max);
   e = launch_kernel(&decode_share_kernel<D, KVT, NU, LONGV>, dim3(p.num_wg), dim3(256),
                     decode_lds_bytes<D>(rows_max, p.num_seqs), stream, p, combine_floats);
   if (e != hipSuccess) return e;

@@ -17,7 +17,8 @@
 // that spans shares go to the workspace as normalised partials with their LSEs
 // and are merged by a second small kernel.
 //
-// Work layout inside a workgroup (4 waves):
+// Work layout inside a workgroup (NW waves: 4 in the decode kernel, 8 in the head_dim-256 mixed
+// kernel):
 //   * the share's chunks are dealt to the waves round-robin.
 //   * per chunk, S^T = K . Q^T on 16x16x32 MFMA (NU sub-tiles of 16 keys; the
 //     16 query rows are the MFMA columns), an online-softmax update in
@@ -36,7 +37,7 @@
 //     to back with no wait in between. Loads past the end of the request are
 //     redirected into its last page (always a valid address) and their values
 //     masked, so no load sits behind a branch.
-//   * the four waves' (max, sum, O) are combined in LDS in a fixed order.
+//   * the NW waves' (max, sum, O) are combined in LDS in a fixed order.
 #pragma once
 
 #include <climits>
@@ -107,11 +108,11 @@ struct DecodeShape {
 };
 
 // One piece of a (request, kv head) unit: chunks [c0, c1) of the unit; the waves start at chunk
-// c0 + first[w] and step by 4 chunks. Rows of a request on this path: r -> (new token r / g,
+// c0 + first[w] and step by NW chunks. Rows of a request on this path: r -> (new token r / g,
 // query head kvh*g + r % g). slot < 0: the piece is the whole unit and is written to out/lse;
 // else it is written to partial slot `slot` of the workspace. LONGV: V page rows are longer than
 // one 32-token half (block size > 32), which decides how the V loads are issued.
-template <int D, int KVT, int NU, bool LONGV>
+template <int D, int KVT, int NU, bool LONGV, int NW>
 __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kvh, int c0, int c1, int wave_first,
                                              int share, int slot, float* lds) {
   constexpr int CH = DecodeShape<NU>::CH;
@@ -214,7 +215,7 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
 
   constexpr int KW = (KVT == KV_BF16) ? KK : KK / 2;    // 16-byte K loads per key row
   typedef typename std::conditional<KVT == KV_BF16, u32x4, u32x2>::type vword;
-  for (; T0 < t_end; T0 += 4 * CH) {
+  for (; T0 < t_end; T0 += NW * CH) {
     // ---------------- issue the K and V loads of this chunk
     u32x4 kraw[NU][KW];
 #pragma unroll
@@ -258,7 +259,7 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
         for (int h = 0; h < NH; ++h) vload(h, n, NH == 2);
     }
     // ---------------- block-table entries of this wave's next chunk
-    const int Tn = T0 + 4 * CH;
+    const int Tn = T0 + NW * CH;
     if (Tn < t_end) {
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
@@ -365,11 +366,11 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
     }
   }
 
-  // ---------------- combine the four waves (fixed order) through LDS.
-  // lds layout: stats[2][4][16] (reference maximum, sum) then O[4][R][D].
+  // ---------------- combine the NW waves (fixed order) through LDS.
+  // lds layout: stats[2][NW][16] (reference maximum, sum) then O[NW][R][D].
   float* smax = lds;
-  float* ssum = lds + 64;
-  float* so = lds + 128;
+  float* ssum = lds + NW * 16;
+  float* so = lds + 2 * NW * 16;
   const float l_row = sum_over_quads(l);
   if (qd == 0) {
     smax[wave * 16 + j] = mc;
@@ -378,11 +379,11 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
   __syncthreads();
   float mx = kNegInf;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) mx = fmaxf(mx, smax[w * 16 + j]);
+  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, smax[w * 16 + j]);
   const float mbase = (mx == kNegInf) ? 0.f : mx;
   float ltot = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const float mw = smax[w * 16 + j];
     ltot += (mw == kNegInf) ? 0.f : ssum[w * 16 + j] * fast_exp2(mw - mbase);
   }
@@ -396,11 +397,11 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
 
   const float row_lse = (ltot == 0.f) ? kNegInf : kLn2 * (mx + fast_log2(ltot));
   if (direct) {
-    for (int idx = tid; idx < R * (D / 4); idx += blockDim.x) {
+    for (int idx = tid; idx < R * (D / 4); idx += NW * 64) {
       const int r = idx / (D / 4), d4 = 4 * (idx - r * (D / 4));
       f32x4 o = *reinterpret_cast<const f32x4*>(so + (0 * R + r) * D + d4);
 #pragma unroll
-      for (int w = 1; w < 4; ++w) o += *reinterpret_cast<const f32x4*>(so + (w * R + r) * D + d4);
+      for (int w = 1; w < NW; ++w) o += *reinterpret_cast<const f32x4*>(so + (w * R + r) * D + d4);
       const int i = r / p.g, h = kvh * p.g + r % p.g;
       *reinterpret_cast<bf16x4*>(p.out + ((size_t)(q0 + i) * p.Hq + h) * D + d4) = f32x4_to_bf16x4(o);
     }
@@ -412,18 +413,19 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
   }
   const size_t unit = (size_t)share * 2 + slot;
   float* wo = p.ws_o + unit * 16 * D;
-  for (int idx = tid; idx < R * (D / 4); idx += blockDim.x) {
+  for (int idx = tid; idx < R * (D / 4); idx += NW * 64) {
     const int r = idx / (D / 4), d4 = 4 * (idx - r * (D / 4));
     f32x4 o = *reinterpret_cast<const f32x4*>(so + (0 * R + r) * D + d4);
 #pragma unroll
-    for (int w = 1; w < 4; ++w) o += *reinterpret_cast<const f32x4*>(so + (w * R + r) * D + d4);
+    for (int w = 1; w < NW; ++w) o += *reinterpret_cast<const f32x4*>(so + (w * R + r) * D + d4);
     *reinterpret_cast<f32x4*>(wo + r * D + d4) = o;
   }
   if (wave == 0 && qd == 0 && j < R) p.ws_lse[unit * 16 + j] = row_lse;
 }
 
-// Exclusive prefix sums of count(b) over requests b < B into sp[0 .. B] (LDS), by all 256
-// threads; thread t scans a contiguous segment of requests. Ends with a barrier.
+// Exclusive prefix sums of count(b) over requests b < B into sp[0 .. B] (LDS); threads 0-255 scan
+// contiguous segments of requests (any further threads of the workgroup have empty segments);
+// wave_tot holds one int per wave of the workgroup. Ends with a barrier.
 template <class Count>
 __device__ __forceinline__ void block_prefix(int B, Count count, int* sp, int* wave_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -449,9 +451,13 @@ __device__ __forceinline__ void block_prefix(int B, Count count, int* sp, int* w
   __syncthreads();
 }
 
-// The partition kernel's body: share g of the batch's chunks walks the (request, kv head)
-// pieces it covers. lds: the combine buffer of decode_piece, then sp[B + 1] and 4 scratch ints.
-template <int D, int KVT, int NU, bool LONGV>
+// The partition kernel's body for a workgroup of NW waves: share g of the batch's chunks walks the
+// (request, kv head) pieces it covers. lds: the combine buffer of decode_piece
+// (decode_combine_floats), then sp[B + 1] and NW scratch ints.
+template <int D, int NW>
+constexpr int decode_combine_floats(int rows) { return 2 * NW * 16 + NW * rows * D; }
+
+template <int D, int KVT, int NU, bool LONGV, int NW = 4>
 __device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, int combine_floats, int g) {
   constexpr int CH = DecodeShape<NU>::CH;
   int* sp = reinterpret_cast<int*>(lds + combine_floats);
@@ -459,7 +465,7 @@ __device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, i
   block_prefix(p.num_seqs, [&](int b) { return decode_chunks<CH>(p, b); }, sp, wave_tot);
   const int B = p.num_seqs, G = p.num_wg;
   if (g == 0)
-    for (int b = threadIdx.x; b <= B; b += blockDim.x) p.ws_prefix[b] = sp[b];
+    for (int b = threadIdx.x; b <= B; b += NW * 64) p.ws_prefix[b] = sp[b];
   const long long T = (long long)p.Hkv * sp[B];
   const long long r0 = share_start(g, T, G), r1 = share_start(g + 1, T, G);
   if (r0 >= r1) return;
@@ -481,9 +487,9 @@ __device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, i
     const int c0 = (int)(pos - base - (long long)kvh * nb);
     const int c1 = (int)min((long long)nb, c0 + (r1 - pos));
     // chunks are dealt to the waves round-robin over the whole share
-    const int wave_first = (int)((wave - (pos - r0) % 4 + 4) % 4);
+    const int wave_first = (int)((wave - (pos - r0) % NW + NW) % NW);
     const int slot = (c0 == 0 && c1 == nb) ? -1 : (first ? 0 : 1);
-    decode_piece<D, KVT, NU, LONGV>(p, b, kvh, c0, c1, wave_first, g, slot, lds);
+    decode_piece<D, KVT, NU, LONGV, NW>(p, b, kvh, c0, c1, wave_first, g, slot, lds);
     pos += c1 - c0;
     first = false;
     if (c1 == nb && kvh == p.Hkv - 1) ++b;

@@ -1,6 +1,7 @@
 // Prefill and mixed-batch kernel instantiations and launchers.
 #include "launch.h"
 #include "prefill_pp.h"
+#include "prefill_pp256.h"
 
 namespace attn {
 
@@ -66,6 +67,36 @@ void varlen_mixed_kernel(PrefillParams pp, PagedParams dp, int n_dec,
   prefill_tile_body<D, BN, Loader, true>(pp, reinterpret_cast<bf16*>(smem_raw), hgrp, lo, qt);
 }
 
+// Mixed varlen batch over a paged cache with head_dim 256: the same one-launch split with 8 waves
+// per workgroup. Decode-share workgroups deal their chunks to 8 waves; prefill workgroups run the
+// ping-pong tile of prefill_pp256.h (128 query rows, two waves per SIMD).
+template <int KVT, int NU, bool LONGV>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void varlen_mixed256_kernel(PrefillParams pp, PagedParams dp, int n_dec, int combine_floats) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  float* lds = reinterpret_cast<float*>(smem_raw);
+  if ((int)blockIdx.x < n_dec) {
+    decode_share<256, KVT, NU, LONGV, 8>(dp, lds, combine_floats, blockIdx.x);
+    return;
+  }
+  const int w = blockIdx.x - n_dec;
+  const int hg = pp.Hkv * (pp.g / pp.hpw);
+  const int hgrp = w % hg, t = w / hg;
+  const int tq = 32 * (4 / pp.hpw);
+  int* sp = reinterpret_cast<int*>(smem_raw + PingPong256Shape<KVT == KV_FP8>::LDS_BYTES);
+  block_prefix(pp.num_seqs, [&](int b) { return prefill_qtiles(pp, b, tq); }, sp, sp + pp.num_seqs + 1);
+  if (t >= sp[pp.num_seqs]) return;
+  int lo = 0, hi = pp.num_seqs - 1;                    // the largest b with sp[b] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sp[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int nt = sp[lo + 1] - sp[lo];
+  const int qt = nt - 1 - (t - sp[lo]);
+  __syncthreads();                                     // sp is not read below; the tile reuses LDS
+  prefill_pp256_body<KVT == KV_FP8>(pp, smem_raw, hgrp, lo, qt);
+}
+
 template <int D, int BN>
 static hipError_t launch_prefill_t(const PrefillParams& p, int max_seqlen, hipStream_t stream) {
   using S = PrefillShape<D, BN>;
@@ -101,19 +132,23 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, 
 }
 
 // Dynamic LDS of the mixed kernel: the larger of the prefill tile buffers and the decode combine
-// buffer, then num_seqs + 5 ints.
-template <int D, int BN>
+// buffer of its NW waves, then num_seqs + 1 + NW ints (prefix sums and per-wave scratch). Head_dim
+// 128: 4 waves and the tiles of prefill_core.h; head_dim 256: 8 waves and the tiles of
+// prefill_pp256.h (the same for both cache dtypes).
+template <int D>
 static size_t mixed_lds_bytes(int num_seqs) {
-  const size_t combine = (size_t)(128 + 4 * 16 * D) * sizeof(float);
-  return std::max((size_t)PrefillShape<D, BN>::LDS_BYTES, combine) + ((size_t)num_seqs + 5) * sizeof(int);
+  constexpr int NW = D == 256 ? 8 : 4;
+  const size_t tiles = D == 256 ? (size_t)PingPong256Shape<false>::LDS_BYTES : (size_t)PrefillShape<D, 64>::LDS_BYTES;
+  const size_t combine = (size_t)decode_combine_floats<D, NW>(16) * sizeof(float);
+  return std::max(tiles, combine) + ((size_t)num_seqs + 1 + NW) * sizeof(int);
 }
 
 // Largest request count whose mixed-kernel LDS fits the 160 KB a workgroup may hold.
 constexpr long long kMaxWorkgroupLds = 160 * 1024;
 template <int D>
 static int mixed_max_seqs_t() {
-  const long long base = (long long)mixed_lds_bytes<D, 64>(0) - 5 * (long long)sizeof(int);
-  return (int)std::min<long long>((kMaxWorkgroupLds - base) / 4 - 5, kMaxPagedSeqs);
+  const long long base = (long long)mixed_lds_bytes<D>(0);
+  return (int)std::min<long long>((kMaxWorkgroupLds - base) / 4, kMaxPagedSeqs);
 }
 
 int mixed_max_seqs(int head_dim) {
@@ -129,14 +164,22 @@ static hipError_t launch_mixed_t(const PrefillParams& pp, const PagedParams& dp,
   if (n_pre + n_dec > 0x7fffffffLL) return hipErrorInvalidValue;
   // both kernels' LDS limits are raised before the first launch
   static std::atomic<bool> done[kMaxDevices];
-  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV>), done,
-                                    (int)mixed_lds_bytes<D, BN>(mixed_max_seqs_t<D>()));
+  const void* fn;
+  if constexpr (D == 256) fn = reinterpret_cast<const void*>(&varlen_mixed256_kernel<KVT, NU, LONGV>);
+  else fn = reinterpret_cast<const void*>(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV>);
+  hipError_t e = ensure_dynamic_lds(fn, done, (int)mixed_lds_bytes<D>(mixed_max_seqs_t<D>()));
   if (e != hipSuccess) return e;
   e = ensure_merge_attrs(D, NU);
   if (e != hipSuccess) return e;
-  const int combine_floats = 128 + 4 * 16 * D;
-  e = launch_kernel(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV>, dim3((unsigned)(n_pre + n_dec)), dim3(256),
-                    mixed_lds_bytes<D, BN>(pp.num_seqs), stream, pp, dp, n_dec, combine_floats);
+  const dim3 grid((unsigned)(n_pre + n_dec));
+  const size_t lds = mixed_lds_bytes<D>(pp.num_seqs);
+  if constexpr (D == 256) {
+    e = launch_kernel(&varlen_mixed256_kernel<KVT, NU, LONGV>, grid, dim3(512), lds, stream, pp, dp, n_dec,
+                      decode_combine_floats<256, 8>(16));
+  } else {
+    e = launch_kernel(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV>, grid, dim3(256), lds, stream, pp, dp, n_dec,
+                      decode_combine_floats<D, 4>(16));
+  }
   if (e != hipSuccess) return e;
   return launch_decode_merge(dp, D, NU, 16, stream);
 }
@@ -150,9 +193,9 @@ static hipError_t launch_mixed_bs(const PrefillParams& pp, const PagedParams& dp
 hipError_t launch_mixed(const PrefillParams& pp, const PagedParams& dp, int head_dim, int kv_type, int total_q,
                         hipStream_t stream) {
   if (head_dim == 128 && kv_type == KV_BF16) return launch_mixed_bs<128, 64, KV_BF16, 4>(pp, dp, total_q, stream);
-  if (head_dim == 256 && kv_type == KV_BF16) return launch_mixed_bs<256, 64, KV_BF16, 2>(pp, dp, total_q, stream);
+  if (head_dim == 256 && kv_type == KV_BF16) return launch_mixed_bs<256, 32, KV_BF16, 2>(pp, dp, total_q, stream);
   if (head_dim == 128 && kv_type == KV_FP8) return launch_mixed_bs<128, 64, KV_FP8, 4>(pp, dp, total_q, stream);
-  if (head_dim == 256 && kv_type == KV_FP8) return launch_mixed_bs<256, 64, KV_FP8, 2>(pp, dp, total_q, stream);
+  if (head_dim == 256 && kv_type == KV_FP8) return launch_mixed_bs<256, 32, KV_FP8, 2>(pp, dp, total_q, stream);
   return hipErrorInvalidValue;
 }
 

@@ -1,6 +1,6 @@
-"""HBM traffic per call of the attention kernels, from hardware counters.
+"""HBM traffic and matrix-core use per call of the attention kernels, from hardware counters.
 
-Two sub-commands:
+Three sub-commands:
 
   python bench_traffic.py copy
       Launches a plain elementwise copy (fp32, 1 GiB read + 1 GiB written, 8 times) and nothing
@@ -13,6 +13,20 @@ Two sub-commands:
       merge kernel of a decode call, the prefill kernel, the mixed kernel and its merge), each
       scaled by the copy's bytes-per-counter factor, summed per call. Each entry records a digest of
       the kernel sources it was measured on; bench.py reports it only while the sources match.
+
+  python bench_traffic.py counters CSV [--kernel FRAGMENT]
+      Prints, for every library kernel in a rocprofv3 counter_collection.csv (or those whose name
+      holds FRAGMENT), the median over its dispatches of each counter collected, and the matrix-core
+      figures derived from them where the counters are present:
+        * MFMA FLOP per dispatch = 512 x (SQ_INSTS_VALU_MFMA_MOPS_BF16 + ..._F8) (each MOPS unit is
+          512 multiply or add operations);
+        * busy cycles = GRBM_GUI_ACTIVE / 8: rocprofv3 sums the counter over the 8 XCDs, each of
+          which counts the dispatch's busy cycles at the graphics clock;
+        * effective clock = busy cycles / the dispatch's duration (its start and end timestamps);
+        * MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (busy cycles x 1024 SIMDs), the figure
+          rocprofv3 derives as MfmaUtil;
+        * achieved MFMA FLOP per busy cycle against the chip's dense peak per cycle (256 compute
+          units x 4096 bf16 FLOP, x 8192 for fp8).
 """
 
 import argparse
@@ -107,16 +121,67 @@ def assemble(a):
         f.write("\n")
 
 
+LIBRARY_KERNELS = ("attn::",)
+XCDS = 8                      # MI355X: GRBM counters are summed over its 8 XCDs
+PEAK_FLOP_PER_CYCLE = {"bf16": 256 * 4096, "fp8": 256 * 8192}
+
+
+def counters(a):
+    """Median per dispatch of each counter, per library kernel, and the derived matrix-core figures."""
+    per = {}
+    with open(a.csv) as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            if not any(k in name for k in LIBRARY_KERNELS) or (a.kernel and a.kernel not in name):
+                continue
+            key = name.split("(")[0]
+            disp = row.get("Dispatch_Id") or row.get("Correlation_Id") or ""
+            c = per.setdefault(key, {}).setdefault(row["Counter_Name"], {})
+            c[disp] = c.get(disp, 0.0) + float(row["Counter_Value"])
+            if row.get("Start_Timestamp") and row.get("End_Timestamp"):
+                per[key].setdefault("_duration_ns", {})[disp] = \
+                    float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+    out = {}
+    for key, cs in per.items():
+        med = {n: statistics.median(d.values()) for n, d in cs.items()}
+        rec = {"dispatches": max(len(d) for d in cs.values()), "median": med}
+        mops = med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + med.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)
+        busy = med["GRBM_GUI_ACTIVE"] / XCDS if "GRBM_GUI_ACTIVE" in med else None
+        if busy:
+            rec["busy_cycles_per_xcd"] = busy
+            if med.get("_duration_ns"):
+                rec["effective_clock_mhz"] = busy / med["_duration_ns"] * 1e3
+        if mops:
+            rec["mfma_flop"] = 512 * mops
+        if busy and "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            rec["mfma_busy_fraction"] = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (busy * 1024)
+        if busy and mops:
+            kind = "fp8" if med.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) > med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) \
+                else "bf16"
+            rec["mfma_flop_per_busy_cycle"] = 512 * mops / busy
+            rec["fraction_of_dense_peak_per_cycle"] = 512 * mops / busy / PEAK_FLOP_PER_CYCLE[kind]
+            rec["peak_kind"] = kind
+        if "SQ_LDS_BANK_CONFLICT" in med and med.get("SQ_LDS_IDX_ACTIVE"):
+            rec["lds_bank_conflict_per_active_cycle"] = med["SQ_LDS_BANK_CONFLICT"] / med["SQ_LDS_IDX_ACTIVE"]
+        out[key] = rec
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     sub.add_parser("copy")
+    cnt = sub.add_parser("counters")
+    cnt.add_argument("csv")
+    cnt.add_argument("--kernel", default=None)
     asm = sub.add_parser("assemble")
     asm.add_argument("--calib", nargs=2, required=True, metavar=("FETCH_CSV", "WRITE_CSV"))
     asm.add_argument("--case", nargs=3, action="append", default=[], metavar=("KEY", "FETCH_CSV", "WRITE_CSV"))
     a = ap.parse_args()
     if a.cmd == "copy":
         run_copy()
+    elif a.cmd == "counters":
+        counters(a)
     else:
         assemble(a)
 

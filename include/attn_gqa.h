@@ -213,8 +213,9 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
  *   q, out [total_q, num_q_heads, head_dim] bf16; lse [total_q, num_q_heads] fp32 or NULL
  *   causal: 0 or 1 (bottom-right aligned)
  *   workspace: >= attn_varlen_workspace_bytes(...) bytes of device scratch.
- * With head_dim 256, num_seqs above 5627 returns ATTN_ERR_UNSUPPORTED (the
- * kernel keeps per-request offsets in LDS beside its 138 KB of tiles).
+ * With head_dim 256, num_seqs above 7927 returns ATTN_ERR_UNSUPPORTED (the
+ * kernel keeps per-request offsets in LDS beside its 129 KB of tiles or
+ * partial results).
  */
 size_t attn_varlen_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t num_splits);

@@ -135,11 +135,12 @@ def test_varlen_validation():
     st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None, 2,
                                10, 5, 8, 2, 128, 16, 10, 4, 1, None, 0, -1, None)
     assert st == 2                                   # negative window
-    # head_dim 256: the mixed kernel's LDS (138 KB of tiles + one int per request) caps num_seqs at 5627
-    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None, 5628,
+    # head_dim 256: the mixed kernel's LDS (129 KB for the 8-wave decode combine buffer + one int per request) caps
+    # num_seqs at 7927
+    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None, 7928,
                                6000, 5, 8, 2, 256, 16, 10, 4, 1, None, 0, 0, None)
     assert st == 3
-    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None, 5627,
+    st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None, 7927,
                                6000, 5, 8, 2, 256, 16, 10, 4, 1, None, 0, 0, None)
     assert st == 4                                   # passes the cap, then no workspace
     st = lib.attn_varlen_paged(FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, 1, 0.1, FAKE, None, 16384,
