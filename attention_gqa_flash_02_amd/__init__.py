@@ -24,6 +24,8 @@ __all__ = [
     "attn_decode_num_splits",
     "attn_decode_workspace_bytes",
     "attn_decode_paged",
+    "attn_decode_paged_noalloc",
+    "ATTN_DECODE_NOALLOC_MAX_BYTES",
     "attn_varlen_workspace_bytes",
     "attn_varlen_paged",
     "attn_kv_append_paged",
@@ -32,6 +34,7 @@ __all__ = [
 
 ATTN_KV_BF16 = 0
 ATTN_KV_FP8_E4M3FN = 1
+ATTN_DECODE_NOALLOC_MAX_BYTES = 16 << 20
 
 
 class AttnError(RuntimeError):
@@ -240,6 +243,35 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale
         kvt, _ptr(k_scale), _ptr(v_scale), int(window), _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_paged")
+    return out, lse
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, scale, k_scale=None, v_scale=None,
+                              out=None, lse=None, num_splits=0, return_lse=True, stream=None, window=0):
+    """attn_decode_paged without a workspace: the partials go to the library's own fixed device
+    array (ATTN_DECODE_NOALLOC_MAX_BYTES per GPU). With out (and lse, or return_lse=False) given,
+    nothing is allocated on this path either."""
+    dev = q.device
+    _check(q, "q", torch.bfloat16, dev)
+    _check_ndim(q, "q", 3)
+    b, hq, d = q.shape
+    kvt, nblk, hkv, bs = _check_caches(k_cache, v_cache, d, dev, k_scale, v_scale)
+    _check(block_table, "block_table", torch.int32, dev)
+    _check_ndim(block_table, "block_table", 2)
+    if block_table.shape[0] != b:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows for {b} requests")
+    _check(seq_lens, "seq_lens", torch.int32, dev, (b,))
+    _check_out(out, lse, (b, hq, d), (b, hq), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((b, hq), dtype=torch.float32, device=dev)
+    st = _lib.load().attn_decode_paged_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), float(scale), _ptr(out),
+        b, hq, hkv, d, bs, nblk, block_table.shape[1], int(num_splits), _ptr(lse),
+        kvt, _ptr(k_scale), _ptr(v_scale), int(window), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_paged_noalloc")
     return out, lse
 
 

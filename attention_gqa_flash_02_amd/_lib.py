@@ -31,6 +31,10 @@ SIGNATURES = {
     "attn_decode_paged": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_f32, c_void_p,
                                   c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_void_p,
                                   c_void_p, c_size, c_i32, c_void_p, c_void_p, c_i32, c_void_p]),
+    # attn_decode_paged without workspace / workspace_bytes
+    "attn_decode_paged_noalloc": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_f32, c_void_p,
+                                          c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_void_p,
+                                          c_i32, c_void_p, c_void_p, c_i32, c_void_p]),
     "attn_varlen_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32]),
     # q, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_table, cu_seqlens_q, seq_lens_k, causal, scale,
     # out, lse, num_seqs, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,

@@ -202,6 +202,34 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
                               void* stream);
 
 /*
+ * attn_decode_paged for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid allocation. It
+ * takes no workspace: the split-KV partials go to a fixed array of
+ * ATTN_DECODE_NOALLOC_MAX_BYTES bytes that the library holds on every GPU it
+ * runs on until the process ends. The call allocates nothing (no hipMalloc, no
+ * allocating library routine); the array's device address is looked up once
+ * per device on the first call there.
+ *   Arguments, layouts, results and validation errors: as attn_decode_paged
+ *   (without workspace / workspace_bytes).
+ *   ATTN_ERR_WORKSPACE: the call would need more than
+ *   ATTN_DECODE_NOALLOC_MAX_BYTES of partials (attn_decode_workspace_bytes of
+ *   its resolved partition count); nothing is launched. The automatic count
+ *   (num_splits = 0) fits every supported shape on MI355X.
+ * Every call on one GPU shares that GPU's array and it keeps the last call's
+ * contents: calls that overlap in time on one GPU (two streams, two host
+ * threads) race and give undefined results. Enqueue them on one stream.
+ */
+#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+
+attn_status attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* seq_lens, float scale, void* out,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t num_splits, float* lse,
+                                      int32_t kv_dtype, const float* k_scale, const float* v_scale,
+                                      int32_t window, void* stream);
+
+/*
  * Mixed varlen batch over a paged cache in one attention launch ("Attention
  * kernels", section "Paged KV and kernels": prefill chunks and decode requests
  * of different lengths in one step). Request b owns query rows
