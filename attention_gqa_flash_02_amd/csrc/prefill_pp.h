@@ -77,6 +77,7 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
   constexpr int NDB = D / 32;       // 32-wide d blocks of O^T
   constexpr int NKK = D / 16;       // k-steps of the QK MFMA
   constexpr float kLazyRescale = 8.f;
+  constexpr float kFastLimit = 4294967296.f;   // 2^32
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: kept in a scalar register
@@ -279,6 +280,37 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
   auto softmax_work = [&](int m) {
       const int n0 = (n_first + m) * BN;
       const bool edge = (n0 + BN > Lk) || (n0 + BN - 1 >= wave_mask_from) || (n0 < wave_lower_max);
+      // Fast path of an interior tile (no masked key) once every row of the wave has a finite
+      // reference maximum: P = 2^(S c - ref) against the current reference, without the tile
+      // maximum. It stands when no lane's tile sum exceeds kFastLimit (then every P of the tile is
+      // below it, far inside the bf16 and fp32 ranges); otherwise the tile is redone below, where
+      // the reference moves. Unless the scores of a row grow by more than 32 / log2(e) after its
+      // first tile, the maximum is taken on the first and the masked tiles only.
+      if (!edge && __builtin_amdgcn_ballot_w64(mc == kNegInf) == 0) {
+        const float nbase = -mc;
+        float ts[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            float e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) e[q] = fast_exp2(__builtin_fmaf(st[kb][8 * t + q], c, nbase));
+#pragma unroll
+            for (int q = 0; q < 8; q += 2) {
+              const bf16x2 pe = cvt_pk_bf16(e[q], e[q + 1]);
+              pB[kb][t][q] = pe[0];
+              pB[kb][t][q + 1] = pe[1];
+            }
+            ts[t] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+          }
+        const float tsum = ts[0] + ts[1];
+        if (__builtin_amdgcn_ballot_w64(!(tsum <= kFastLimit)) == 0) {
+          l += tsum;
+          pedge = false;
+          return;
+        }
+      }
       if (edge) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
