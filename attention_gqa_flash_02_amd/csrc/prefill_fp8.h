@@ -261,6 +261,28 @@ __device__ __forceinline__ void prefill_fp8_body(const PrefillFp8Params& p, unsi
     const int n0 = (n_first + m) * BN;
     const bool edge = (n0 + BN > Lk) || (n0 + BN - 1 >= wave_mask_from) || (n0 < wave_lower_max);
     const bool split = edge || (n0 < wave_split_end);
+    // Fast path of an unsplit interior tile once every row of the wave has a finite reference
+    // maximum: P = 2^(S c - ref) without the tile maximum, kept unless some lane's tile sum
+    // exceeds 2^8 (so every P stays at most 2^8, inside e4m3's range; else the tile is redone
+    // below, where the reference moves).
+    if (!split && __builtin_amdgcn_ballot_w64(mc == kNegInf) == 0) {
+      const float nbase = -mc;
+      float tsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 2 * NKB * 2; ++w) {
+        const int kb = w / 4, r = 4 * (w % 4);
+        float e[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) e[q] = fast_exp2(__builtin_fmaf(st[kb][r + q], c, nbase));
+        pB[w] = pack_fp8x4(e[0], e[1], e[2], e[3]);
+        tsum += (e[0] + e[1]) + (e[2] + e[3]);
+      }
+      if (__builtin_amdgcn_ballot_w64(!(tsum <= 256.f)) == 0) {
+        l += tsum;
+        psplit = false;
+        return;
+      }
+    }
     if (edge) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)

@@ -65,6 +65,7 @@ __device__ __forceinline__ void prefill_pp256_body(const PrefillParams& p, unsig
   constexpr int VPL = 16 / ELT;     // values per 16-byte load
   constexpr int NL = S::LOADS;      // 16-byte loads per staging thread per tile
   constexpr float kLazyRescale = 8.f;
+  constexpr float kFastLimit = 4294967296.f;   // 2^32: far inside the bf16 and fp32 ranges
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -290,6 +291,31 @@ __device__ __forceinline__ void prefill_pp256_body(const PrefillParams& p, unsig
   auto softmax_work = [&](int m) {
     const int n0 = (n_first + m) * BN;
     const bool edge = (n0 + BN > Lk) || (n0 + BN - 1 >= wave_mask_from) || (n0 < wave_lower_max);
+    // Fast path of an interior tile once every row of the wave has a finite reference maximum:
+    // P = 2^(S c - ref) without the tile maximum, kept unless some lane's tile sum exceeds
+    // kFastLimit (then the tile is redone below, where the reference moves).
+    if (!edge && __builtin_amdgcn_ballot_w64(mc == kNegInf) == 0) {
+      const float nbase = -mc;
+      float tsum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = fast_exp2(__builtin_fmaf(st[8 * t + q], c, nbase));
+#pragma unroll
+        for (int q = 0; q < 8; q += 2) {
+          const bf16x2 pe = cvt_pk_bf16(e[q], e[q + 1]);
+          pB[t][q] = pe[0];
+          pB[t][q + 1] = pe[1];
+        }
+        tsum += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      }
+      if (__builtin_amdgcn_ballot_w64(!(tsum <= kFastLimit)) == 0) {
+        l += tsum;
+        pedge = false;
+        return;
+      }
+    }
     if (edge) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
