@@ -67,9 +67,24 @@ def sources_digest(names):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(key, sources):
+# Per traffic case: the kernel-name fragments of one library call, and the sources they are built from.
+TRAFFIC_CASES = {
+    "decode_paged_c2": (["decode_share_kernel", "decode_merge_kernel"], ["common.h", "decode_core.h", "decode.hip"]),
+    "decode_c4": (["decode_share_kernel", "decode_merge_kernel"], ["common.h", "decode_core.h", "decode.hip"]),
+    "prefill_c3": (["prefill_pingpong_kernel"], ["common.h", "prefill_core.h", "prefill_pp.h", "prefill.hip"]),
+    "prefill_c3_fp8": (["prefill_fp8_kernel"], ["common.h", "prefill_core.h", "prefill_pp.h", "prefill_fp8.h",
+                                                 "prefill_fp8.hip"]),
+    "append_c5": (["kv_append_kernel"], ["common.h", "append.hip"]),
+    "mixed_c5": (["varlen_mixed256_kernel", "decode_merge_kernel"],
+                 ["common.h", "decode_core.h", "decode.hip", "prefill_core.h", "prefill_pp.h", "prefill_pp256.h",
+                  "prefill.hip"]),
+}
+
+
+def measured_traffic(key):
     """HBM bytes per call from profiles/traffic.json (FETCH_SIZE + WRITE_SIZE of the kernels of one
     call, scaled by a copy-kernel calibration), or None when absent or measured on other sources."""
+    sources = TRAFFIC_CASES[key][1]
     try:
         with open(TRAFFIC_FILE) as f:
             entry = json.load(f).get(key)
@@ -85,96 +100,6 @@ def measured_traffic(key, sources):
 WARM_MS = 50.0
 
 
-class GpuClock:
-    """Reads the graphics clock of the benchmarked GPU through amdsmi (matched to torch's device by
-    PCI bus id), on a background thread while a section warms up. Any failure leaves it disabled
-    and is reported instead of a clock."""
-
-    def __init__(self, dev_index=0):
-        self.handle = None
-        self.error = None
-        try:
-            import amdsmi
-            import torch
-            self.amdsmi = amdsmi
-            amdsmi.amdsmi_init()
-            props = torch.cuda.get_device_properties(dev_index)
-            want = (getattr(props, "pci_domain_id", 0), getattr(props, "pci_bus_id", None),
-                    getattr(props, "pci_device_id", None))
-            handles = amdsmi.amdsmi_get_processor_handles()
-            for h in handles:
-                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)        # "dddd:bb:dd.f"
-                dom, bus, rest = bdf.split(":")
-                if want[1] is None or (int(bus, 16) == want[1] and int(dom, 16) == want[0]):
-                    self.handle = h
-                    break
-            if self.handle is None and len(handles) == 1:
-                self.handle = handles[0]
-            if self.handle is None:
-                self.error = f"no amdsmi device matches PCI bus {want}"
-            else:
-                self.read()
-        except Exception as e:                                  # no amdsmi, no permission, ...
-            self.handle = None
-            self.error = repr(e)[:200]
-
-    def read(self):
-        """Current graphics clock in MHz (amdsmi clock_info; the gpu_metrics table, which can lag
-        by tens of milliseconds, only if that fails)."""
-        a = self.amdsmi
-        try:
-            return float(a.amdsmi_get_clock_info(self.handle, a.AmdSmiClkType.GFX)["clk"])
-        except Exception:
-            m = a.amdsmi_get_gpu_metrics_info(self.handle)
-            clks = [int(c) for c in m.get("current_gfxclks", []) if isinstance(c, (int, float)) and 0 < c < 10000]
-            return sum(clks) / len(clks)
-
-    def sampler(self):
-        return _ClockSampler(self)
-
-
-class _ClockSampler:
-    def __init__(self, clock):
-        self.clock = clock
-        self.samples = []
-        self.stop = False
-        self.thread = None
-
-    def __enter__(self):
-        import threading
-        if self.clock.handle is None:
-            return self
-
-        def run():
-            while not self.stop:
-                try:
-                    self.samples.append((time.perf_counter(), self.clock.read()))
-                except Exception:
-                    return
-                time.sleep(0.004)
-        self.thread = threading.Thread(target=run, daemon=True)
-        self.thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self.stop = True
-        if self.thread is not None:
-            self.thread.join()
-        return False
-
-    def summary(self, since):
-        if self.clock.handle is None:
-            return {"error": self.clock.error}
-        xs = [c for t, c in self.samples if t >= since] or [c for _, c in self.samples]
-        if not xs:
-            return {"error": "no sample"}
-        return {"mean": round(sum(xs) / len(xs), 1), "min": min(xs), "max": max(xs), "samples": len(xs),
-                "when": "second half of the warm-up (the GPU runs the same workload back to back)"}
-
-
-CLOCK = None
-
-
 def time_steps(fns, steps, warmup):
     """Run fns round-robin: at least `warmup` calls and at least WARM_MS of GPU time untimed (the host
     synchronises every few calls, so the elapsed time is GPU time), then `steps` timed calls between
@@ -183,18 +108,16 @@ def time_steps(fns, steps, warmup):
     import torch
     n = len(fns)
     torch.cuda.synchronize()
-    sampler = CLOCK.sampler() if CLOCK is not None else None
     calls = 0
     t0 = time.perf_counter()
-    with (sampler if sampler is not None else _NullCtx()):
-        while True:
-            fns[calls % n]()
-            calls += 1
-            if calls % 4 == 0 or calls >= warmup:
-                torch.cuda.synchronize()
-                elapsed = (time.perf_counter() - t0) * 1e3
-                if calls >= warmup and elapsed >= WARM_MS:
-                    break
+    while True:
+        fns[calls % n]()
+        calls += 1
+        if calls % 4 == 0 or calls >= warmup:
+            torch.cuda.synchronize()
+            elapsed = (time.perf_counter() - t0) * 1e3
+            if calls >= warmup and elapsed >= WARM_MS:
+                break
     warm_ms = (time.perf_counter() - t0) * 1e3
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -211,17 +134,7 @@ def time_steps(fns, steps, warmup):
     info = {"timed_calls": steps, "mean_ms": statistics.mean(durs), "median_ms": statistics.median(durs),
             "min_ms": min(durs), "max_ms": max(durs), "wall_ms_per_call": wall,
             "warmup_calls": calls, "warmup_ms": round(warm_ms, 2)}
-    if sampler is not None:
-        info["gfx_clock_mhz"] = sampler.summary(t0 + warm_ms / 2e3)
     return wall, durs, info
-
-
-class _NullCtx:
-    def __enter__(self):
-        return self
-
-    def __exit__(self, *exc):
-        return False
 
 
 def to_device(case, dev):
@@ -388,7 +301,7 @@ def append_section(lib, steps, warmup):
             "tokens": tn, "bytes": nbytes, "ms": kern, "wall_ms": wall, "gbs": gbs, "timing": info,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("append_c5", ["append.hip"])}}
+                         "traffic": measured_traffic("append_c5")}}
 
 
 def parity_stats(out, lse, ref_o, ref_l):
@@ -465,9 +378,6 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] device: {torch.cuda.get_device_name(dev)}; library {lib.library_path()}")
-    global CLOCK
-    CLOCK = GpuClock(0)
-    log(f"[bench] clock readings: {'amdsmi' if CLOCK.handle is not None else CLOCK.error}")
     run = (lambda name: a.only is None or a.only == name)
     extra = {}
 
@@ -513,7 +423,7 @@ def main():
             "tflops": tf, "ms": pre["kernel_ms_mean"], "wall_ms": pre["wall_ms"], "timing": pre["timing"],
             "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tf / MFMA_BF16_PEAK_TFS,
-                         "traffic": measured_traffic("prefill_c3", ["common.h", "prefill_core.h", "prefill_pp.h", "prefill.hip"])},
+                         "traffic": measured_traffic("prefill_c3")},
             "algorithmic_flops": pre["flops"]}
         if not a.quick:
             units = [(0, 0), (1, 7), (2, 19), (3, 31)]
@@ -546,8 +456,7 @@ def main():
             "timing": pf["timing"],
             "roofline": {"bound": "mfma", "achieved": tf8, "peak": MFMA_FP8_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tf8 / MFMA_FP8_PEAK_TFS,
-                         "traffic": measured_traffic("prefill_c3_fp8", ["common.h", "prefill_core.h", "prefill_pp.h",
-                                                                        "prefill_fp8.h", "prefill_fp8.hip"])}}
+                         "traffic": measured_traffic("prefill_c3_fp8")}}
         if not a.quick:
             units = [(0, 0), (1, 7), (2, 19), (3, 31)]
             par = sampled_parity_prefill_fp8(c3f, pf["out"], pf["lse"], units)
@@ -569,7 +478,7 @@ def main():
             "gbs": gbs, "partitions": best["splits"], "ms": best["kernel_ms_mean"], "timing": best["timing"],
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("decode_c4", ["common.h", "decode_core.h", "decode.hip"])}}
+                         "traffic": measured_traffic("decode_c4")}}
         if not a.quick:
             units = [(0, 0), (1, 17), (0, 31)]
             par = sampled_parity_paged(c4, best["out"], best["lse"], units)
@@ -592,8 +501,7 @@ def main():
             "algorithmic_flops": mx["flops"], "decode_kv_bytes": mx["decode_kv_bytes"],
             "prefill_kv_bytes": mx["prefill_kv_bytes"],
             "roofline": {"bound": "mfma", "lower_bound_ms": mx["t_star_ms"], "frac": mx["t_star_ms"] / mx["ms"],
-                         "traffic": measured_traffic("mixed_c5", ["common.h", "decode_core.h", "decode.hip",
-                                                                  "prefill_core.h", "prefill_pp.h", "prefill.hip"])}}
+                         "traffic": measured_traffic("mixed_c5")}}
         if not a.quick:
             n_pre = sum(1 for ql in c5.q_lens if ql > 1)
             units = [(0, 0), (n_pre - 1, 15), (n_pre, 3), (n_pre + 50, 9), (len(c5.q_lens) - 1, 12)]
@@ -636,7 +544,7 @@ def main():
                        "kv_bytes": dec["kv_bytes"], "parallelism": "single GPU"},
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic("decode_paged_c2", ["common.h", "decode_core.h", "decode.hip"])},
+                         "traffic": measured_traffic("decode_paged_c2")},
         })
     else:
         line.update({"value": None, "ms_per_step": None,

@@ -42,19 +42,6 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_ELEMS = 1 << 28          # fp32 elements: 1 GiB each way
 COPY_REPS = 8
 
-# per case: the kernel-name fragments of one call, and the sources the kernels are built from
-CASES = {
-    "decode_paged_c2": (["decode_share_kernel", "decode_merge_kernel"], ["common.h", "decode_core.h", "decode.hip"]),
-    "decode_c4": (["decode_share_kernel", "decode_merge_kernel"], ["common.h", "decode_core.h", "decode.hip"]),
-    "prefill_c3": (["prefill_pingpong_kernel"], ["common.h", "prefill_core.h", "prefill_pp.h", "prefill.hip"]),
-    "prefill_c3_fp8": (["prefill_fp8_kernel"], ["common.h", "prefill_core.h", "prefill_pp.h", "prefill_fp8.h",
-                                                 "prefill_fp8.hip"]),
-    "append_c5": (["kv_append_kernel"], ["append.hip"]),
-    "mixed_c5": (["varlen_mixed_kernel", "decode_merge_kernel"],
-                 ["common.h", "decode_core.h", "decode.hip", "prefill_core.h", "prefill_pp.h", "prefill.hip"]),
-}
-
-
 def run_copy():
     import torch
     dev = torch.device("cuda:0")
@@ -87,7 +74,7 @@ def pick(per, fragment):
 
 def assemble(a):
     sys.path.insert(0, ROOT)
-    from bench import sources_digest
+    from bench import sources_digest, TRAFFIC_CASES as CASES
     f_fetch = pick(read_counter(a.calib[0], "FETCH_SIZE"), "elementwise")
     f_write = pick(read_counter(a.calib[1], "WRITE_SIZE"), "elementwise")
     nbytes = 4 * COPY_ELEMS
