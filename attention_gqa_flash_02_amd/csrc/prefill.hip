@@ -21,12 +21,29 @@ void prefill_varlen_kernel(PrefillParams p) {
 }
 
 // Varlen self-attention over contiguous K/V with head_dim 128: the ping-pong kernel (8 waves,
-// 96 KB of LDS: three 16 KB buffers each of K and V; one workgroup per compute unit). Grid as above; a q-tile is 32 * 8 / hpw rows.
+// 96 KB of LDS: three 16 KB buffers each of K and V; one workgroup per compute unit); a q-tile is
+// 32 * 8 / hpw rows. One-dimensional grid over (head group, request, q-tile). The dispatcher deals
+// workgroup i to XCD i % 8; when the (head group, request) pairs are a multiple of 8, XCD x takes
+// pairs x, x + 8, ... one after the other, each pair's q-tiles heaviest first, so that the
+// workgroups an XCD runs at once stream the same K/V tiles through its L2. Otherwise the order is
+// (head group, request) fastest, q-tiles heaviest first.
 template <int BN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_pingpong_kernel(PrefillParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  prefill_pingpong_body<BN>(p, smem_raw, blockIdx.x, blockIdx.y, p.num_qtiles - 1 - (int)blockIdx.z);
+  const int id = blockIdx.x;
+  const int HG = p.Hkv * (p.g / p.hpw), Z = p.num_qtiles;
+  const int P = HG * p.num_seqs;
+  int pair, t;
+  if (P % 8 == 0) {
+    const int k = id >> 3;
+    pair = (id & 7) + 8 * (k / Z);
+    t = k % Z;
+  } else {
+    pair = id % P;
+    t = id / P;
+  }
+  prefill_pingpong_body<BN>(p, smem_raw, pair % HG, pair / HG, Z - 1 - t);
 }
 
 // Q-tiles of request b on the prefill path of a mixed batch (its rows do not fit the decode path).
@@ -121,8 +138,9 @@ static hipError_t launch_pingpong_t(const PrefillParams& p, int max_seqlen, hipS
   PrefillParams q = p;
   q.num_qtiles = (max_seqlen + tq - 1) / tq;
   if (q.num_qtiles <= 0) return hipSuccess;
-  dim3 grid(p.Hkv * (p.g / p.hpw), p.num_seqs, q.num_qtiles);
-  return launch_kernel(&prefill_pingpong_kernel<BN>, grid, dim3(512), S::LDS_BYTES, stream, q);
+  const long long n = (long long)p.Hkv * (p.g / p.hpw) * p.num_seqs * q.num_qtiles;
+  if (n > 0x7fffffffLL) return hipErrorInvalidValue;
+  return launch_kernel(&prefill_pingpong_kernel<BN>, dim3((unsigned)n), dim3(512), S::LDS_BYTES, stream, q);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, hipStream_t stream) {
