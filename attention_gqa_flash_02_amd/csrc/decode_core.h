@@ -247,14 +247,17 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
       if constexpr (KVT == KV_BF16) vraw[h][n] = nt ? ld16nt(vrow) : ld16(vrow);
       else vraw[h][n] = nt ? ld8nt(vrow) : ld8(vrow);
     };
+    // With head_dim 256, bf16 pages and 8 waves (256 registers per lane), the second half of the
+    // V loads is issued after the QK products, in the registers the K rows leave free.
+    constexpr int NB_EARLY = (D == 256 && KVT == KV_BF16 && NW == 8) ? NB / 2 : NB;
     if constexpr (!LONGV) {
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int n = 0; n < NB; ++n) vload(h, n, true);
+        for (int n = 0; n < NB_EARLY; ++n) vload(h, n, true);
     } else {
 #pragma unroll
-      for (int n = 0; n < NB; ++n)
+      for (int n = 0; n < NB_EARLY; ++n)
 #pragma unroll
         for (int h = 0; h < NH; ++h) vload(h, n, NH == 2);
     }
@@ -284,6 +287,12 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
         }
       }
       st[u] = a * c;
+    }
+    if constexpr (NB_EARLY < NB) {
+#pragma unroll
+      for (int n = NB_EARLY; n < NB; ++n)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) vload(h, n, !LONGV || NH == 2);
     }
     // A chunk is a tail chunk when some row may not see all of its keys (the end of the request,
     // the causal edge of a multi-token request, or the start of a sliding window). Only tail chunks mask scores, zero V slots

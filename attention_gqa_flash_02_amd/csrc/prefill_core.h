@@ -183,6 +183,11 @@ struct PagedLoader {
   static constexpr int V_CH = BN / VPL;             // 16-byte loads per V^T d row of the tile
   static constexpr int V_LOADS = D * V_CH / 256;
   static_assert(K_LOADS >= 1 && V_LOADS >= 1 && BN * K_CH % 256 == 0 && D * V_CH % 256 == 0, "tile split");
+  // K: thread t loads K_LOADS consecutive 16-byte chunks of key row t / K_TPR (one page, so one
+  // block-table entry); V: thread t loads VPL-key runs starting at the same key for V_LOADS d rows
+  // (again one page).
+  static constexpr int K_TPR = 256 / BN;            // threads per K row
+  static_assert(256 % BN == 0 && K_TPR * K_LOADS == K_CH && 256 % V_CH == 0, "one page per thread");
   u32x4 kreg[K_LOADS];
   u32x4 vreg[V_LOADS];
   const char* kc;
@@ -204,38 +209,35 @@ struct PagedLoader {
   }
   // Block-table entries are loaded one tile ahead of the K/V loads that use them, so a fetch
   // never waits on a table load.
-  int kphys[K_LOADS], vphys[V_LOADS];
+  int kphys, vphys;
   int tile0;
   __device__ __forceinline__ void load_table(int n) {
     const int tid = threadIdx.x;
     const int n0 = n * BN;
     const int last = Lk - 1;
-#pragma unroll
-    for (int it = 0; it < K_LOADS; ++it) kphys[it] = table[min(n0 + (it * 256 + tid) / K_CH, last) >> bs_shift];
-#pragma unroll
-    for (int it = 0; it < V_LOADS; ++it) {
-      const int t0 = n0 + VPL * ((it * 256 + tid) % V_CH);
-      vphys[it] = table[min(t0, last & ~(VPL - 1)) >> bs_shift];
-    }
+    kphys = table[min(n0 + tid / K_TPR, last) >> bs_shift];
+    vphys = table[min(n0 + VPL * (tid % V_CH), last & ~(VPL - 1)) >> bs_shift];
   }
   __device__ __forceinline__ void fetch(int n) {                // table entries of tile n are loaded
     const int tid = threadIdx.x;
     const int n0 = n * BN;
     tile0 = n0;
     const int last = Lk - 1;
+    {
+      const int key = min(n0 + tid / K_TPR, last);
+      const char* row = kc + (size_t)kphys * block_stride + (size_t)(key & (bs - 1)) * D * ELT +
+                        16 * K_LOADS * (tid % K_TPR);
 #pragma unroll
-    for (int it = 0; it < K_LOADS; ++it) {
-      const int idx = it * 256 + tid;
-      const int key = min(n0 + idx / K_CH, last), ch = idx % K_CH;
-      const char* row = kc + (size_t)kphys[it] * block_stride + (size_t)(key & (bs - 1)) * D * ELT;
-      kreg[it] = ld16(row + 16 * ch);                 // rows past the keys are zeroed in stage
+      for (int it = 0; it < K_LOADS; ++it) kreg[it] = ld16(row + 16 * it);   // rows past the keys are zeroed in stage
     }
+    {
+      const int tt = min(n0 + VPL * (tid % V_CH), last & ~(VPL - 1));   // a VPL-aligned run inside a valid page
+      const char* col = vc + (size_t)vphys * block_stride + (size_t)(tt & (bs - 1)) * ELT;
 #pragma unroll
-    for (int it = 0; it < V_LOADS; ++it) {
-      const int idx = it * 256 + tid;
-      const int d = idx / V_CH, t0 = n0 + VPL * (idx % V_CH);
-      const int tt = min(t0, last & ~(VPL - 1));          // a VPL-aligned run inside a valid page
-      vreg[it] = ld16(vc + (size_t)vphys[it] * block_stride + ((size_t)d * bs + (tt & (bs - 1))) * ELT);
+      for (int it = 0; it < V_LOADS; ++it) {
+        const int d = (it * 256 + tid) / V_CH;
+        vreg[it] = ld16(col + (size_t)d * bs * ELT);
+      }
     }
     if ((n + 1) * BN < Lk) load_table(n + 1);
   }
@@ -243,9 +245,10 @@ struct PagedLoader {
     using S = PrefillShape<D, BN>;
     const int tid = threadIdx.x;
     if (tile0 + BN > Lk) {                          // the last tile: zero keys past the end
+      if (tile0 + tid / K_TPR >= Lk) {
 #pragma unroll
-      for (int it = 0; it < K_LOADS; ++it)
-        if (tile0 + (it * 256 + tid) / K_CH >= Lk) kreg[it] = u32x4{0, 0, 0, 0};
+        for (int it = 0; it < K_LOADS; ++it) kreg[it] = u32x4{0, 0, 0, 0};
+      }
 #pragma unroll
       for (int it = 0; it < V_LOADS; ++it) {
         const int t0 = tile0 + VPL * ((it * 256 + tid) % V_CH);
@@ -263,8 +266,7 @@ struct PagedLoader {
     }
 #pragma unroll
     for (int it = 0; it < K_LOADS; ++it) {
-      const int idx = it * 256 + tid;
-      const int key = idx / K_CH, ch = idx % K_CH;
+      const int key = tid / K_TPR, ch = K_LOADS * (tid % K_TPR) + it;
       bf16* dst = Ks + key * S::KS + VPL * ch;
       if constexpr (FP8) {
         *reinterpret_cast<bf16x8*>(dst) = fp8x8_to_bf16x8(kreg[it][0], kreg[it][1]);
@@ -484,11 +486,15 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
     __syncthreads();
   }
 
-  // ---- epilogue: O / l (bf16, round to nearest even) and the natural-log LSE
+  // ---- epilogue: O / l (bf16, round to nearest even) and the natural-log LSE. The output row
+  // index is taken through an empty asm, so that its address is computed here rather than kept
+  // live (in registers the tile loop needs) from before the loop.
   const float l_row = l + __shfl_xor(l, 32, kWave);
+  int orow_i = q0 + qrow_i;
+  asm volatile("" : "+v"(orow_i));
   if (wave_active && qrow_i < Lq) {
     const float inv = (l_row > 0.f) ? vscale / l_row : 0.f;
-    bf16* orow = p.out + ((size_t)(q0 + qrow_i) * p.Hq + head) * D;
+    bf16* orow = p.out + ((size_t)orow_i * p.Hq + head) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -497,7 +503,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillParams& p, bf16* 
         *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * rb + 4 * hh) = f32x4_to_bf16x4(o4);
       }
     if (p.lse && hh == 0)
-      p.lse[(size_t)(q0 + qrow_i) * p.Hq + head] = (l_row > 0.f) ? kLn2 * (mc + fast_log2(l_row)) : kNegInf;
+      p.lse[(size_t)orow_i * p.Hq + head] = (l_row > 0.f) ? kLn2 * (mc + fast_log2(l_row)) : kNegInf;
   }
 }
 
