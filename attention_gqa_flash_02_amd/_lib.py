@@ -4,7 +4,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libattn_gqa.so")
+# ATTN_GQA_LIBRARY names another build of the same library to load instead (the host-ASan build of
+# the validation tests).
+LIB_PATH = os.environ.get("ATTN_GQA_LIBRARY") or os.path.join(_PKG, "lib", "libattn_gqa.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "attn_gqa.h")
 
 c_void_p = ctypes.c_void_p
