@@ -22,6 +22,8 @@
 //     cache). Every other row (the first and last rows of a request, a decode token, a chunk cut by
 //     the workgroup boundary) is written element by element, so that no slot outside the new rows
 //     is touched.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace attn {
@@ -40,12 +42,32 @@ __device__ int request_of_row_global(const int32_t* cu, int B, int row) {
   return lo;
 }
 
-// fp32 -> e4m3fn codes of x / s for 4 values, packed little-endian into one word
-__device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x3, float s) {
-  const float q0 = fminf(fmaxf(x0 / s, -448.f), 448.f);
-  const float q1 = fminf(fmaxf(x1 / s, -448.f), 448.f);
-  const float q2 = fminf(fmaxf(x2 / s, -448.f), 448.f);
-  const float q3 = fminf(fmaxf(x3 / s, -448.f), 448.f);
+// x / s in fp32, correctly rounded. FAST: without a division per value (Markstein's method,
+// "Handbook of Floating-Point Arithmetic", division by a correctly rounded reciprocal): with
+// r = 1/s correctly rounded, q = x r is within one ulp of x / s, the residual q s - x is exact in
+// one fma, and q - (q s - x) r rounded once is the correctly rounded quotient, as long as nothing
+// under- or overflows. The caller takes FAST only for scales in [2^-60, 2^60]: the e4m3 code
+// depends on the exact quotient only for |x / s| from 2^-10 (half the smallest subnormal) up,
+// where then |x| >= 2^-70 and the residual stays a normal number. Quotients past 1024 only need
+// their sign (they saturate to 448): q is clamped there first, so nothing overflows to a NaN.
+// Written as q - (q s - x) r, a zero x keeps its sign.
+template <bool FAST>
+__device__ __forceinline__ float quotient(float x, float s, float r) {
+  if constexpr (!FAST) {
+    return x / s;
+  } else {
+    const float q = __builtin_amdgcn_fmed3f(x * r, -1024.f, 1024.f);
+    return __builtin_fmaf(-__builtin_fmaf(q, s, -x), r, q);
+  }
+}
+
+// fp32 -> e4m3fn codes of x / s for 4 values (saturated at 448), packed little-endian into one word
+template <bool FAST>
+__device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x3, float s, float r) {
+  const float q0 = __builtin_amdgcn_fmed3f(quotient<FAST>(x0, s, r), -448.f, 448.f);
+  const float q1 = __builtin_amdgcn_fmed3f(quotient<FAST>(x1, s, r), -448.f, 448.f);
+  const float q2 = __builtin_amdgcn_fmed3f(quotient<FAST>(x2, s, r), -448.f, 448.f);
+  const float q3 = __builtin_amdgcn_fmed3f(quotient<FAST>(x3, s, r), -448.f, 448.f);
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
   return (uint32_t)w;
@@ -171,78 +193,86 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   const int nfull = s_cnt[0];
   const int npart = s_cnt[1];
 
-  // ---- K: each item (16 values of one row) becomes one 16-byte fp8 piece or two bf16 pieces
-  const float ks = FP8 ? p.k_scale[h] : 1.f;
+  // ---- the stores. Quantisation without a division per value needs scales in [2^-60, 2^60]
+  // (see quotient); the choice is uniform over the workgroup.
+  const float ks = FP8 ? p.k_scale[h] : 1.f, vs = FP8 ? p.v_scale[h] : 1.f;
+  const float kr = 1.f / ks, vr = 1.f / vs;
+  auto in_range = [](float x) { return x >= 0x1p-60f && x <= 0x1p60f; };
+  auto emit = [&](auto fast_c) {
+    constexpr bool F = decltype(fast_c)::value;
+    // ---- K: each item (16 values of one row) becomes one 16-byte fp8 piece or two bf16 pieces
 #pragma unroll
-  for (int u = 0; u < ITEMS; ++u) {
-    const int i = tid + 256 * u, r = i / IPR, c = i % IPR;
-    if (r >= nrows) continue;
-    char* dst = reinterpret_cast<char*>(p.k_cache) +
-                (((size_t)s_page[r] * p.bs + (s_pos[r] & (p.bs - 1))) * D + 16 * c) * ELT;
-    if constexpr (!FP8) {
-      *reinterpret_cast<u32x4*>(dst) = kin[u][0];
-      *reinterpret_cast<u32x4*>(dst + 16) = kin[u][1];
-    } else {
-      const u32x4 a = kin[u][0], e = kin[u][1];
-      u32x4 o;
-      o[0] = quant4(bf16_lo(a[0]), bf16_hi(a[0]), bf16_lo(a[1]), bf16_hi(a[1]), ks);
-      o[1] = quant4(bf16_lo(a[2]), bf16_hi(a[2]), bf16_lo(a[3]), bf16_hi(a[3]), ks);
-      o[2] = quant4(bf16_lo(e[0]), bf16_hi(e[0]), bf16_lo(e[1]), bf16_hi(e[1]), ks);
-      o[3] = quant4(bf16_lo(e[2]), bf16_hi(e[2]), bf16_lo(e[3]), bf16_hi(e[3]), ks);
-      *reinterpret_cast<u32x4*>(dst) = o;
+    for (int u = 0; u < ITEMS; ++u) {
+      const int i = tid + 256 * u, r = i / IPR, c = i % IPR;
+      if (r >= nrows) continue;
+      char* dst = reinterpret_cast<char*>(p.k_cache) +
+                  (((size_t)s_page[r] * p.bs + (s_pos[r] & (p.bs - 1))) * D + 16 * c) * ELT;
+      if constexpr (!FP8) {
+        *reinterpret_cast<u32x4*>(dst) = kin[u][0];
+        *reinterpret_cast<u32x4*>(dst + 16) = kin[u][1];
+      } else {
+        const u32x4 a = kin[u][0], e = kin[u][1];
+        u32x4 o;
+        o[0] = quant4<F>(bf16_lo(a[0]), bf16_hi(a[0]), bf16_lo(a[1]), bf16_hi(a[1]), ks, kr);
+        o[1] = quant4<F>(bf16_lo(a[2]), bf16_hi(a[2]), bf16_lo(a[3]), bf16_hi(a[3]), ks, kr);
+        o[2] = quant4<F>(bf16_lo(e[0]), bf16_hi(e[0]), bf16_lo(e[1]), bf16_hi(e[1]), ks, kr);
+        o[3] = quant4<F>(bf16_lo(e[2]), bf16_hi(e[2]), bf16_lo(e[3]), bf16_hi(e[3]), ks, kr);
+        *reinterpret_cast<u32x4*>(dst) = o;
+      }
     }
-  }
 
-  // ---- V, whole chunks: (chunk, head_dim pair) items
-  const float vs = FP8 ? p.v_scale[h] : 1.f;
-  for (int it = tid; it < nfull * HD; it += 256) {
-    const int i0 = s_full[it / HD], d = 2 * (it % HD);
-    uint32_t w[16];                                           // bf16 pairs (d, d + 1) of the 16 rows
+    // ---- V, whole chunks: (chunk, head_dim pair) items
+    for (int it = tid; it < nfull * HD; it += 256) {
+      const int i0 = s_full[it / HD], d = 2 * (it % HD);
+      uint32_t w[16];                                           // bf16 pairs (d, d + 1) of the 16 rows
 #pragma unroll
-    for (int t = 0; t < 16; ++t) w[t] = *reinterpret_cast<const uint32_t*>(s_v + (i0 + t) * VS + d);
-    const size_t e0 = ((size_t)s_page[i0] * D + d) * p.bs + (s_pos[i0] & (p.bs - 1));   // (d, first slot)
-    if constexpr (!FP8) {
-      bf16* v0 = reinterpret_cast<bf16*>(p.v_cache) + e0;
-      bf16* v1 = v0 + p.bs;                                   // the d + 1 row
+      for (int t = 0; t < 16; ++t) w[t] = *reinterpret_cast<const uint32_t*>(s_v + (i0 + t) * VS + d);
+      const size_t e0 = ((size_t)s_page[i0] * D + d) * p.bs + (s_pos[i0] & (p.bs - 1));   // (d, first slot)
+      if constexpr (!FP8) {
+        bf16* v0 = reinterpret_cast<bf16*>(p.v_cache) + e0;
+        bf16* v1 = v0 + p.bs;                                   // the d + 1 row
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        u32x4 lo4, hi4;
+        for (int q = 0; q < 2; ++q) {
+          u32x4 lo4, hi4;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t x0 = w[8 * q + 2 * c], x1 = w[8 * q + 2 * c + 1];
+            lo4[c] = (x0 & 0xffffu) | (x1 << 16);               // d row: slots 2c, 2c + 1
+            hi4[c] = (x0 >> 16) | (x1 & 0xffff0000u);           // d + 1 row
+          }
+          *reinterpret_cast<u32x4*>(v0 + 8 * q) = lo4;
+          *reinterpret_cast<u32x4*>(v1 + 8 * q) = hi4;
+        }
+      } else {
+        uint8_t* v0 = reinterpret_cast<uint8_t*>(p.v_cache) + e0;
+        uint32_t q0[4], q1[4];                                  // codes of the d and d + 1 rows
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t x0 = w[8 * q + 2 * c], x1 = w[8 * q + 2 * c + 1];
-          lo4[c] = (x0 & 0xffffu) | (x1 << 16);               // d row: slots 2c, 2c + 1
-          hi4[c] = (x0 >> 16) | (x1 & 0xffff0000u);           // d + 1 row
+          q0[c] = quant4<F>(bf16_lo(w[4 * c]), bf16_lo(w[4 * c + 1]), bf16_lo(w[4 * c + 2]), bf16_lo(w[4 * c + 3]), vs, vr);
+          q1[c] = quant4<F>(bf16_hi(w[4 * c]), bf16_hi(w[4 * c + 1]), bf16_hi(w[4 * c + 2]), bf16_hi(w[4 * c + 3]), vs, vr);
         }
-        *reinterpret_cast<u32x4*>(v0 + 8 * q) = lo4;
-        *reinterpret_cast<u32x4*>(v1 + 8 * q) = hi4;
+        *reinterpret_cast<u32x4*>(v0) = u32x4{q0[0], q0[1], q0[2], q0[3]};
+        *reinterpret_cast<u32x4*>(v0 + p.bs) = u32x4{q1[0], q1[1], q1[2], q1[3]};
       }
-    } else {
-      uint8_t* v0 = reinterpret_cast<uint8_t*>(p.v_cache) + e0;
-      uint32_t q0[4], q1[4];                                  // codes of the d and d + 1 rows
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        q0[c] = quant4(bf16_lo(w[4 * c]), bf16_lo(w[4 * c + 1]), bf16_lo(w[4 * c + 2]), bf16_lo(w[4 * c + 3]), vs);
-        q1[c] = quant4(bf16_hi(w[4 * c]), bf16_hi(w[4 * c + 1]), bf16_hi(w[4 * c + 2]), bf16_hi(w[4 * c + 3]), vs);
-      }
-      *reinterpret_cast<u32x4*>(v0) = u32x4{q0[0], q0[1], q0[2], q0[3]};
-      *reinterpret_cast<u32x4*>(v0 + p.bs) = u32x4{q1[0], q1[1], q1[2], q1[3]};
     }
-  }
 
-  // ---- V, the other rows: (row, head_dim pair) items
-  for (int it = tid; it < npart * HD; it += 256) {
-    const int r = s_prow[it / HD], d = 2 * (it % HD);
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(s_v + r * VS + d);
-    const size_t e0 = ((size_t)s_page[r] * D + d) * p.bs + (s_pos[r] & (p.bs - 1));
-    if constexpr (!FP8) {
-      reinterpret_cast<uint16_t*>(p.v_cache)[e0] = (uint16_t)(w & 0xffffu);
-      reinterpret_cast<uint16_t*>(p.v_cache)[e0 + p.bs] = (uint16_t)(w >> 16);
-    } else {
-      const uint32_t q = quant4(bf16_lo(w), bf16_hi(w), 0.f, 0.f, vs);
-      reinterpret_cast<uint8_t*>(p.v_cache)[e0] = (uint8_t)(q & 0xffu);
-      reinterpret_cast<uint8_t*>(p.v_cache)[e0 + p.bs] = (uint8_t)((q >> 8) & 0xffu);
+    // ---- V, the other rows: (row, head_dim pair) items
+    for (int it = tid; it < npart * HD; it += 256) {
+      const int r = s_prow[it / HD], d = 2 * (it % HD);
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(s_v + r * VS + d);
+      const size_t e0 = ((size_t)s_page[r] * D + d) * p.bs + (s_pos[r] & (p.bs - 1));
+      if constexpr (!FP8) {
+        reinterpret_cast<uint16_t*>(p.v_cache)[e0] = (uint16_t)(w & 0xffffu);
+        reinterpret_cast<uint16_t*>(p.v_cache)[e0 + p.bs] = (uint16_t)(w >> 16);
+      } else {
+        const uint32_t q = quant4<F>(bf16_lo(w), bf16_hi(w), 0.f, 0.f, vs, vr);
+        reinterpret_cast<uint8_t*>(p.v_cache)[e0] = (uint8_t)(q & 0xffu);
+        reinterpret_cast<uint8_t*>(p.v_cache)[e0 + p.bs] = (uint8_t)((q >> 8) & 0xffu);
+      }
     }
-  }
+  };
+  if (in_range(ks) && in_range(vs)) emit(std::true_type{});
+  else emit(std::false_type{});
   (void)lane;
 }
 
