@@ -241,8 +241,9 @@ def mixed_section(lib, case, steps, warmup):
 
 def multi_token_section(lib, case, steps, warmup, q_len=4):
     """Speculative-verification decode on the batch-32 cache: each request's last q_len cached
-    tokens are new query rows (g * q_len = 16 rows per KV head, one decode-path partition set),
-    through the mixed varlen call. Algorithmic bytes: the K/V bytes, as for the decode."""
+    tokens are new query rows, through the mixed varlen call (up to 16 rows per KV head, g * q_len,
+    take the split-KV decode path; more take the prefill tiles). Algorithmic bytes: the K/V bytes,
+    as for the decode."""
     import torch
     from attention_gqa_flash_02_amd import workmodel
     dev = case.q.device
@@ -262,8 +263,10 @@ def multi_token_section(lib, case, steps, warmup, q_len=4):
     kern = statistics.mean(durs)
     gbs = kv_bytes / kern / 1e6
     log(f"[bench] multi-token decode q_len={q_len}: call mean={kern * 1e3:.1f} us -> {gbs:.0f} GB/s")
+    rows = hq // case.num_kv_heads * q_len
+    path = "split-KV decode path" if rows <= 16 else "prefill tiles"
     return {"workload": f"batch-32 paged decode cache (32/8 heads, D 128, bf16, 16-token pages), {q_len} new "
-                        f"query rows per request (g * q_len = 16 rows per KV head)",
+                        f"query rows per request ({rows} rows per KV head: {path})",
             "q_len": q_len, "kv_bytes": kv_bytes, "ms": kern, "wall_ms": wall, "gbs": gbs, "timing": info,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
@@ -398,6 +401,7 @@ def main():
             extra["decode_parity_sample"] = par
         extra["decode_c2_timing"] = dec["timing"]
         extra["multi_token_decode"] = multi_token_section(lib, c2, a.steps, a.warmup)
+        extra["multi_token_decode_q8"] = multi_token_section(lib, c2, a.steps, a.warmup, q_len=8)
         del c2
         torch.cuda.empty_cache()
 
