@@ -10,11 +10,13 @@
 // each group per SIMD, and takes 128 query rows: 4 row blocks of 32 rows (a row block = 32 tokens of
 // one query head; the heads of a block set share one KV head, so every K/V tile in LDS serves all
 // of them). A row block belongs to a pair of waves of one group (waves 2p and 2p+1 of the group):
-// both hold the block's Q^T (the whole head_dim) and compute the same S^T = K Q^T and softmax; each
-// accumulates one half of O^T (head_dim 0-127 or 128-255). At head_dim 256 a wave cannot hold
-// Q^T (64 registers), S^T, P and all of O^T (128) within the 256 registers of two waves per SIMD;
-// splitting O keeps every wave at two per SIMD, at the price of computing S^T twice (the matrix
-// work per useful FLOP is 1.5x).
+// both hold the block's Q^T (the whole head_dim) and compute the same S^T = K Q^T; each accumulates
+// one half of O^T (head_dim 0-127 or 128-255). At head_dim 256 a wave cannot hold Q^T (64
+// registers), S^T, P and all of O^T (128) within the 256 registers of two waves per SIMD; splitting
+// O keeps every wave at two per SIMD, at the price of computing S^T twice (the matrix work per
+// useful FLOP is 1.5x). The exponentials are not computed twice: each wave of a pair takes the
+// tile's row maximum from the whole S^T but computes P only for its own 16 of the 32 keys, and the
+// two halves of P meet in LDS, which shortens the vector work of the slot that sets the pace.
 //
 // Ping-pong (as in prefill_pp.h). Time is cut into slots that end at a workgroup barrier. In each
 // slot one group runs its matrix work (P V of its previous tile, then S^T of its current tile)
@@ -48,7 +50,9 @@ struct PingPong256Shape {
   static constexpr int K_BYTES = BN * KS * 2;       // one K tile
   static constexpr int V_BYTES = D * VS * 2;        // one V^T tile
   static constexpr int NBUF = 3;
-  static constexpr int LDS_BYTES = NBUF * (K_BYTES + V_BYTES);
+  static constexpr int XCHG_OFFSET = NBUF * (K_BYTES + V_BYTES);
+  static constexpr int XCHG_BYTES = 2 * 8 * 64 * 16;       // P half (hi, lo) per wave and lane
+  static constexpr int LDS_BYTES = XCHG_OFFSET + XCHG_BYTES;
   static constexpr int ELT = FP8 ? 1 : 2;
   static constexpr int LOADS = 32 * ELT / 16;       // 16-byte loads per staging thread per tile
 };
@@ -206,9 +210,13 @@ __device__ __forceinline__ void prefill_pp256_body(const PrefillParams& p, unsig
     }
   };
 
-  // ---- operand addresses inside a tile (bytes)
-  const int kaddr = key_perm32(j) * S::KS * 2 + 16 * hh;                 // + 32 * kk
-  const int vaddr = (128 * dh + j) * S::VS * 2 + 16 * hh;               // + 32 * db * VS * 2 + 32 * t
+  // ---- operand addresses inside a tile (bytes). The second wave of a pair takes the tile's two
+  // 16-key halves in swapped order (A row i of its S^T is key key_perm32(i) ^ 16), so in both waves
+  // score slots 0-7 and P half 0 belong to the wave's own keys 16 dh .. 16 dh + 15, and P half t
+  // multiplies the V^T columns of key half t ^ dh.
+  const int kaddr = (key_perm32(j) ^ (16 * dh)) * S::KS * 2 + 16 * hh;  // + 32 * kk
+  const int vbase = (128 * dh + j) * S::VS * 2 + 16 * hh;
+  const int vaddr[2] = {vbase + 32 * dh, vbase + 32 * (dh ^ 1)};         // + 32 * db * VS * 2
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -241,6 +249,10 @@ __device__ __forceinline__ void prefill_pp256_body(const PrefillParams& p, unsig
 #pragma unroll
   for (int t = 0; t < 2; ++t) pB[t] = pL[t] = bf16x8{};
   bool pedge = false;
+  // P halves of the wave pairs: [hi, lo][wave][lane]. Each wave writes the half of its own keys in
+  // its softmax slot and reads its partner's in its next matrix slot (a workgroup barrier between).
+  bf16x8* const xp = reinterpret_cast<bf16x8*>(smem + S::XCHG_OFFSET);
+  const int xown = wave * 64 + lane, xother = (wave ^ 1) * 64 + lane;
 
   // Matrix slot: P V of tile m-1 (8 MFMAs on the wave's half of O^T) and S^T of tile m (16 MFMAs),
   // V and K operands interleaved one to two and read AHEAD operands in advance
@@ -250,7 +262,7 @@ __device__ __forceinline__ void prefill_pp256_body(const PrefillParams& p, unsig
   constexpr int NOP = NV + NK;
   constexpr int AHEAD = 6;
   auto is_v = [](int i) { return i % 3 == 0; };
-  auto matrix_slot = [&](auto kb_c) {
+  auto matrix_slot = [&](auto kb_c, bool has_p) {
     constexpr int KB = decltype(kb_c)::value;           // K (m) is in buffer m % 3
     constexpr int VB = (KB + 2) % 3;                    // V (m-1)
     const unsigned char* Ks = kbuf0 + KB * S::K_BYTES;
@@ -258,11 +270,15 @@ __device__ __forceinline__ void prefill_pp256_body(const PrefillParams& p, unsig
     auto fetch = [&](int i) -> bf16x8 {
       if (is_v(i)) {
         const int v = i / 3, db = v >> 1, t = v & 1;
-        return *reinterpret_cast<const bf16x8*>(Vt + vaddr + db * 32 * S::VS * 2 + 32 * t);
+        return *reinterpret_cast<const bf16x8*>(Vt + vaddr[t] + db * 32 * S::VS * 2);
       }
       const int kk = i - i / 3 - 1;
       return *reinterpret_cast<const bf16x8*>(Ks + kaddr + 32 * kk);
     };
+    if (has_p) {                      // the partner's half of P (m-1)
+      pB[1] = xp[xother];
+      if (pedge) pL[1] = xp[512 + xother];
+    }
     bf16x8 ring[AHEAD];
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) ring[i] = fetch(i);
@@ -283,43 +299,22 @@ __device__ __forceinline__ void prefill_pp256_body(const PrefillParams& p, unsig
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const int db = v >> 1, t = v & 1;
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vt + vaddr + db * 32 * S::VS * 2 + 32 * t);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vt + vaddr[t] + db * 32 * S::VS * 2);
         acc[db] = mfma_32x32x16(va, pL[t], acc[db]);
       }
     }
   };
+  // Softmax of tile m: masks (edge tiles), the tile's row maximum over all 32 keys and the lazy
+  // reference move (both waves of a pair hold the same S^T, so they take the same decisions), then
+  // P for the wave's own 16 keys only (hi + lo parts on edge tiles), written for the partner. The
+  // row sum l takes the own keys; the partner's l holds the others.
   auto softmax_work = [&](int m) {
     const int n0 = (n_first + m) * BN;
     const bool edge = (n0 + BN > Lk) || (n0 + BN - 1 >= wave_mask_from) || (n0 < wave_lower_max);
-    // Fast path of an interior tile once every row of the wave has a finite reference maximum:
-    // P = 2^(S c - ref) without the tile maximum, kept unless some lane's tile sum exceeds
-    // kFastLimit (then the tile is redone below, where the reference moves).
-    if (!edge && __builtin_amdgcn_ballot_w64(mc == kNegInf) == 0) {
-      const float nbase = -mc;
-      float tsum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float e[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = fast_exp2(__builtin_fmaf(st[8 * t + q], c, nbase));
-#pragma unroll
-        for (int q = 0; q < 8; q += 2) {
-          const bf16x2 pe = cvt_pk_bf16(e[q], e[q + 1]);
-          pB[t][q] = pe[0];
-          pB[t][q + 1] = pe[1];
-        }
-        tsum += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-      }
-      if (__builtin_amdgcn_ballot_w64(!(tsum <= kFastLimit)) == 0) {
-        l += tsum;
-        pedge = false;
-        return;
-      }
-    }
     if (edge) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = n0 + 16 * (r >> 3) + 8 * hh + (r & 7);
+        const int key = n0 + 16 * ((r >> 3) ^ dh) + 8 * hh + (r & 7);
         st[r] = (key <= lim && key >= lower) ? st[r] : kNegInf;
       }
     }
@@ -338,31 +333,28 @@ __device__ __forceinline__ void prefill_pp256_body(const PrefillParams& p, unsig
     }
     const float nbase = (mc == kNegInf) ? 0.f : -mc;
     if (!edge) {
+      float e[8];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float e[8];
+      for (int q = 0; q < 8; ++q) e[q] = fast_exp2(__builtin_fmaf(st[q], c, nbase));
 #pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = fast_exp2(__builtin_fmaf(st[8 * t + q], c, nbase));
-#pragma unroll
-        for (int q = 0; q < 8; q += 2) {
-          const bf16x2 pe = cvt_pk_bf16(e[q], e[q + 1]);
-          pB[t][q] = pe[0];
-          pB[t][q + 1] = pe[1];
-        }
-        l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      for (int q = 0; q < 8; q += 2) {
+        const bf16x2 pe = cvt_pk_bf16(e[q], e[q + 1]);
+        pB[0][q] = pe[0];
+        pB[0][q + 1] = pe[1];
       }
+      l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
     } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float x = st[8 * t + q];
-          const float e = (x == kNegInf) ? 0.f : fast_exp2(__builtin_fmaf(x, c, nbase));
-          l += e;
-          pB[t][q] = (bf16)e;
-          pL[t][q] = (bf16)(e - (float)pB[t][q]);
-        }
+      for (int q = 0; q < 8; ++q) {
+        const float x = st[q];
+        const float e = (x == kNegInf) ? 0.f : fast_exp2(__builtin_fmaf(x, c, nbase));
+        l += e;
+        pB[0][q] = (bf16)e;
+        pL[0][q] = (bf16)(e - (float)pB[0][q]);
+      }
+      xp[512 + xown] = pL[0];
     }
+    xp[xown] = pB[0];
     pedge = edge;
   };
 
@@ -374,7 +366,7 @@ __device__ __forceinline__ void prefill_pp256_body(const PrefillParams& p, unsig
       constexpr int KB = decltype(kb_c)::value;
       if (m > N) return;
       __builtin_amdgcn_s_setprio(1);
-      matrix_slot(kb_c);
+      matrix_slot(kb_c, m > 0);
       __builtin_amdgcn_s_setprio(0);
       __syncthreads();
       if (m < N) softmax_work(m);
@@ -397,7 +389,7 @@ __device__ __forceinline__ void prefill_pp256_body(const PrefillParams& p, unsig
       constexpr int KB = decltype(kb_c)::value;
       if (m > N) return;
       __builtin_amdgcn_s_setprio(1);
-      matrix_slot(kb_c);
+      matrix_slot(kb_c, m > 0);
       __builtin_amdgcn_s_setprio(0);
       __syncthreads();
       if (m < N) softmax_work(m);
@@ -412,9 +404,15 @@ __device__ __forceinline__ void prefill_pp256_body(const PrefillParams& p, unsig
     }
   }
 
-  // ---- epilogue: this wave's half of O / l (bf16, round to nearest even); the natural-log LSE from
-  // the first wave of the pair
-  const float l_row = l + __shfl_xor(l, 32, kWave);
+  // ---- epilogue: the row sums of the pair's two key halves are added through LDS; then this
+  // wave's half of O / l (bf16, round to nearest even) and the natural-log LSE from the first wave
+  // of the pair
+  float* const xl = reinterpret_cast<float*>(smem + S::XCHG_OFFSET);    // [wave][lane]
+  const float l_half = l + __shfl_xor(l, 32, kWave);
+  __syncthreads();                    // the last matrix slot's reads of the exchange area are done
+  xl[xown] = l_half;
+  __syncthreads();
+  const float l_row = l_half + xl[xother];
   if (wave_active && qrow_i < Lq) {
     const float inv = (l_row > 0.f) ? vscale / l_row : 0.f;
     bf16* orow = p.out + ((size_t)(q0 + qrow_i) * p.Hq + head) * D + 128 * dh;
