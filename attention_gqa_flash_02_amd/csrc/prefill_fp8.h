@@ -256,24 +256,37 @@ __device__ __forceinline__ void prefill_fp8_body(const PrefillFp8Params& p, unsi
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[db] = mfma_f8_32x32x64(vop[db], pL, acc[db]);
     }
+    // The scores go into the exponent domain of the current reference here, t = S c - ref (S c
+    // while a row has none): the matrix slot has room to spare, the softmax slot beside it sets the
+    // pace. (The empty asm keeps each product in this slot; the compiler would otherwise sink it
+    // past the barrier.)
+    const float tb = (mc == kNegInf) ? 0.f : -mc;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = __builtin_fmaf(st[kb][r], c, tb);
+        asm volatile("" : "+v"(x));
+        st[kb][r] = x;
+      }
   };
   auto softmax_work = [&](int m) {
     const int n0 = (n_first + m) * BN;
     const bool edge = (n0 + BN > Lk) || (n0 + BN - 1 >= wave_mask_from) || (n0 < wave_lower_max);
     const bool split = edge || (n0 < wave_split_end);
+    const float tb = (mc == kNegInf) ? 0.f : -mc;    // st holds t = S c + tb (see the matrix slot)
     // Fast path of an unsplit interior tile once every row of the wave has a finite reference
-    // maximum: P = 2^(S c - ref) without the tile maximum, kept unless some lane's tile sum
-    // exceeds 2^8 (so every P stays at most 2^8, inside e4m3's range; else the tile is redone
-    // below, where the reference moves).
+    // maximum: P = 2^t without the tile maximum, kept unless some lane's tile sum exceeds 2^8 (so
+    // every P stays at most 2^8, inside e4m3's range; else the tile is redone below, where the
+    // reference moves).
     if (!split && __builtin_amdgcn_ballot_w64(mc == kNegInf) == 0) {
-      const float nbase = -mc;
       float tsum = 0.f;
 #pragma unroll
       for (int w = 0; w < 2 * NKB * 2; ++w) {
         const int kb = w / 4, r = 4 * (w % 4);
         float e[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) e[q] = fast_exp2(__builtin_fmaf(st[kb][r + q], c, nbase));
+        for (int q = 0; q < 4; ++q) e[q] = fast_exp2(st[kb][r + q]);
         pB[w] = pack_fp8x4(e[0], e[1], e[2], e[3]);
         tsum += (e[0] + e[1]) + (e[2] + e[3]);
       }
@@ -292,29 +305,30 @@ __device__ __forceinline__ void prefill_fp8_body(const PrefillFp8Params& p, unsi
           st[kb][r] = (key <= lim && key >= lower) ? st[kb][r] : kNegInf;
         }
     }
+    // tile maximum in t units; the reference moves where it exceeds the current one by more than
+    // kLazyRescale (any finite maximum where the row has no reference yet)
     float tmax = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) tmax = max3(tmax, st[kb][r], st[kb][r + 1]);
     tmax = max_with_other_half(tmax);
-    tmax = (tmax == kNegInf) ? kNegInf : tmax * c;
-    const bool move = tmax > mc + kLazyRescale;
+    const bool move = tmax > ((mc == kNegInf) ? kNegInf : kLazyRescale);
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
-      const float alpha = move ? ((mc == kNegInf) ? 0.f : fast_exp2(mc - tmax)) : 1.f;
-      mc = move ? tmax : mc;
+      const float alpha = move ? ((mc == kNegInf) ? 0.f : fast_exp2(-tmax)) : 1.f;
+      mc = move ? tmax - tb : mc;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
     }
-    const float nbase = (mc == kNegInf) ? 0.f : -mc;
+    const float sh = move ? tmax : 0.f;             // t - sh is relative to the (new) reference
     if (!split) {
 #pragma unroll
       for (int w = 0; w < 2 * NKB * 2; ++w) {       // dword w of the B operand: scores 4w .. 4w+3
         const int kb = w / 4, r = 4 * (w % 4);
         float e[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) e[q] = fast_exp2(__builtin_fmaf(st[kb][r + q], c, nbase));
+        for (int q = 0; q < 4; ++q) e[q] = fast_exp2(st[kb][r + q] - sh);
         pB[w] = pack_fp8x4(e[0], e[1], e[2], e[3]);
         l += (e[0] + e[1]) + (e[2] + e[3]);
       }
@@ -326,7 +340,7 @@ __device__ __forceinline__ void prefill_fp8_body(const PrefillFp8Params& p, unsi
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float x = st[kb][r + q];
-          e[q] = (x == kNegInf) ? 0.f : fast_exp2(__builtin_fmaf(x, c, nbase));
+          e[q] = (x == kNegInf) ? 0.f : fast_exp2(x - sh);
         }
         const int hi = pack_fp8x4(e[0], e[1], e[2], e[3]);
         const f32x2 d01 = unpack_fp8x2<false>(hi), d23 = unpack_fp8x2<true>(hi);
