@@ -231,14 +231,21 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   p.max_blocks = max_blocks_per_seq;
   p.num_wg = S;
   p.causal = 1;
+  p.max_rows = 16;
   hipError_t e = launch_decode(p, head_dim, kv_dtype == ATTN_KV_BF16 ? KV_BF16 : KV_FP8, g,
                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+// Rows of a partial-result slot in the mixed batch's workspace: the most rows per (request, kv
+// head) that its decode role takes (32 with head_dim 128, 16 with head_dim 256).
+static int varlen_slot_rows(int32_t head_dim) { return head_dim == 128 ? 32 : 16; }
+
 size_t attn_varlen_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t num_splits) {
-  return attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, num_splits);
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
+  return (size_t)num_splits * 2 * varlen_slot_rows(head_dim) * ((size_t)head_dim + 1) * sizeof(float) +
+         ((size_t)num_seqs + 1) * sizeof(int32_t);
 }
 
 attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
@@ -278,9 +285,12 @@ attn_status attn_varlen_paged(const void* q, const void* k_cache, const void* v_
   dp.cu_seqlens_q = cu_seqlens_q;
   dp.out = static_cast<bf16*>(out);
   dp.lse = lse;
+  // requests with up to 16 rows per kv head (32 with head_dim 128 when some request has more
+  // than 16) take the decode role; the workspace slots have that many rows
+  dp.max_rows = ((long long)max_q_len * g > 16 && varlen_slot_rows(head_dim) >= 32) ? 32 : 16;
   dp.ws_o = static_cast<float*>(workspace);
-  dp.ws_lse = dp.ws_o + (size_t)S * 2 * 16 * head_dim;
-  dp.ws_prefix = reinterpret_cast<int32_t*>(dp.ws_lse + (size_t)S * 2 * 16);
+  dp.ws_lse = dp.ws_o + (size_t)S * 2 * dp.max_rows * head_dim;
+  dp.ws_prefix = reinterpret_cast<int32_t*>(dp.ws_lse + (size_t)S * 2 * dp.max_rows);
   dp.scale = scale;
   dp.window = window;
   dp.num_seqs = num_seqs;

@@ -2,7 +2,8 @@
 //
 // What it computes ("Attention kernels", section "Prefill and decode attention"):
 // the few query rows of a request that share one KV head (g query heads x Lq
-// new tokens, at most 16 rows) attend over the request's paged cache; each KV
+// new tokens, at most 16 rows, or 32 in the head_dim-128 mixed batch) attend over the
+// request's paged cache; each KV
 // head is read once for all of them, and the key axis is cut into pieces whose
 // results are merged with their log-sum-exps (the same rule as the online
 // softmax). Pages are located through the block table ("Optimization 1",
@@ -20,8 +21,8 @@
 // Work layout inside a workgroup (NW waves: 4 in the decode kernel, 8 in the head_dim-256 mixed
 // kernel):
 //   * the share's chunks are dealt to the waves round-robin.
-//   * per chunk, S^T = K . Q^T on 16x16x32 MFMA (NU sub-tiles of 16 keys; the
-//     16 query rows are the MFMA columns), an online-softmax update in
+//   * per chunk, S^T = K . Q^T on 16x16x32 MFMA (NU sub-tiles of 16 keys; each
+//     block of 16 query rows is the MFMA columns), an online-softmax update in
 //     registers, then O^T += V^T . P^T on 16x16x32 MFMA. V pages are stored
 //     token-innermost ([D][block_size]), so the V^T operand comes straight from
 //     HBM with the key axis contiguous in each lane; P^T is the S^T accumulator
@@ -60,11 +61,13 @@ struct PagedParams {
   const int32_t* cu_seqlens_q; // [B + 1], or nullptr: request b owns q row b
   bf16* out;                   // [Tq, Hq, D]
   float* lse;                  // [Tq, Hq] or nullptr
-  float* ws_o;                 // [G, 2, 16, D] partial outputs (normalised)
-  float* ws_lse;               // [G, 2, 16] partial natural-log LSEs
+  float* ws_o;                 // [G, 2, max_rows, D] partial outputs (normalised)
+  float* ws_lse;               // [G, 2, max_rows] partial natural-log LSEs
   int32_t* ws_prefix;          // [B + 1] chunk-count prefix sums, written by workgroup 0
   float scale;
   int num_seqs, Hq, Hkv, g, bs, max_blocks, num_wg, causal;
+  int max_rows;                // 16 or 32: most query rows of one (request, kv head) on this path,
+                               // and the rows of a workspace slot
   int window;                  // > 0: row i of a request also drops keys j < len - qlen + i - window + 1
   int bs_shift;                // log2(bs): block sizes are powers of two
 };
@@ -82,7 +85,7 @@ __device__ __forceinline__ int decode_chunks(const PagedParams& p, int b) {
   const int len = p.seq_lens_k[b];
   const int qlen = p.cu_seqlens_q ? (p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b]) : 1;
   const int rows = qlen * p.g;
-  if (!(rows > 0 && rows <= 16)) return 0;
+  if (!(rows > 0 && rows <= p.max_rows)) return 0;
   // chunks from the one holding the first visible key (chunk indices of a unit count from there)
   return (len + CH - 1) / CH - decode_key_begin(p, len, qlen) / CH;
 }
@@ -111,8 +114,10 @@ struct DecodeShape {
 // c0 + first[w] and step by NW chunks. Rows of a request on this path: r -> (new token r / g,
 // query head kvh*g + r % g). slot < 0: the piece is the whole unit and is written to out/lse;
 // else it is written to partial slot `slot` of the workspace. LONGV: V page rows are longer than
-// one 32-token half (block size > 32), which decides how the V loads are issued.
-template <int D, int KVT, int NU, bool LONGV, int NW>
+// one 32-token half (block size > 32), which decides how the V loads are issued. NR: blocks of 16
+// rows (1, or 2 for up to 32 rows: several new tokens of a request at group size 4 and up); each K
+// and V operand is loaded and converted once and feeds the MFMAs of every row block.
+template <int D, int KVT, int NU, bool LONGV, int NW, int NR = 1>
 __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kvh, int c0, int c1, int wave_first,
                                              int share, int slot, float* lds) {
   constexpr int CH = DecodeShape<NU>::CH;
@@ -139,15 +144,16 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
   const float c = p.scale * kscale * kLog2e;           // base-2 exponent per raw score unit
   constexpr float kLazyRescale = 8.f;                  // see the running statistics below
 
-  // ---- Q^T operands (B of the QK MFMA): lane (j = row, qd) holds Q[row][d-slots].
-  bf16x8 qB[KK];
-  int limit;                                          // last visible key of row j
-  int lower;                                          // first visible key of row j
-  {
-    const int r = j;
+  // ---- Q^T operands (B of the QK MFMA): lane (j, qd) holds Q[row 16 rb + j][d-slots].
+  bf16x8 qB[NR][KK];
+  int limit[NR];                                      // last visible key of row 16 rb + j
+  int lower[NR];                                      // first visible key of row 16 rb + j
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb) {
+    const int r = 16 * rb + j;
     const int i = (r < R) ? r / p.g : 0;
-    limit = p.causal ? (len - qlen + i) : (len - 1);
-    lower = p.window > 0 ? (len - qlen + i - p.window + 1) : INT_MIN;
+    limit[rb] = p.causal ? (len - qlen + i) : (len - 1);
+    lower[rb] = p.window > 0 ? (len - qlen + i - p.window + 1) : INT_MIN;
     if (r < R) {
       const int h = kvh * p.g + (r % p.g);
       const bf16* qrow = p.q + ((size_t)(q0 + i) * p.Hq + h) * D;
@@ -156,28 +162,34 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
         // bf16 cache: natural d order; fp8 cache: d = 64*(kk/2) + 16*qd + 8*(kk%2), so one
         // 16-byte fp8 load feeds two MFMAs. Q uses the same order as K.
         const int d0 = (KVT == KV_BF16) ? (32 * kk + 8 * qd) : (64 * (kk >> 1) + 16 * qd + 8 * (kk & 1));
-        qB[kk] = *reinterpret_cast<const bf16x8*>(qrow + d0);
+        qB[rb][kk] = *reinterpret_cast<const bf16x8*>(qrow + d0);
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) qB[kk] = bf16x8{};
+      for (int kk = 0; kk < KK; ++kk) qB[rb][kk] = bf16x8{};
     }
-    // An empty asm redefines the Q registers: their loads are waited for here, once, so the
-    // chunk loop never waits on the memory counter for them (which would also wait for the
-    // chunk's own K/V loads issued after them).
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(qB[kk]));
   }
+  // An empty asm redefines the Q registers: their loads are waited for here, once, so the
+  // chunk loop never waits on the memory counter for them (which would also wait for the
+  // chunk's own K/V loads issued after them).
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(qB[rb][kk]));
 
   // Running statistics of row j, in the base-2 exponent domain t = c * s: mc is a reference
   // maximum (the same in all four quads), l this lane's share of sum 2^(t - mc). The reference
   // is only moved when a row's maximum exceeds it by more than kLazyRescale (so P <= 2^8 and
   // the O rescale is skipped on almost every chunk); any reference gives the same result.
-  float mc = kNegInf;
-  float l = 0.f;
-  f32x4 acc[NB];            // O^T[16n + 4qd + r][row j], scaled by 2^-mc
+  float mc[NR], l[NR];
+  f32x4 acc[NR][NB];        // O^T[16n + 4qd + r][row 16 rb + j], scaled by 2^-mc
 #pragma unroll
-  for (int n = 0; n < NB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < NR; ++rb) {
+    mc[rb] = kNegInf;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[rb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const size_t page_bytes = (size_t)p.bs * D * ELT;   // bytes per (block, kv head) page
   const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
@@ -272,21 +284,33 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
     }
 
     // ---------------- S^T = K . Q^T for the NU sub-tiles, in exponent units t = c * s.
-    f32x4 st[NU];
+    f32x4 st[NR][NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 a[NR];
+#pragma unroll
+      for (int rb = 0; rb < NR; ++rb) a[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (KVT == KV_BF16) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) a = mfma_16x16x32(bitcast<bf16x8>(kraw[u][kk]), qB[kk], a);
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 ka = bitcast<bf16x8>(kraw[u][kk]);
+#pragma unroll
+          for (int rb = 0; rb < NR; ++rb) a[rb] = mfma_16x16x32(ka, qB[rb][kk], a[rb]);
+        }
       } else {
 #pragma unroll
         for (int w = 0; w < KW; ++w) {
-          a = mfma_16x16x32(fp8x8_to_bf16x8(kraw[u][w][0], kraw[u][w][1]), qB[2 * w], a);
-          a = mfma_16x16x32(fp8x8_to_bf16x8(kraw[u][w][2], kraw[u][w][3]), qB[2 * w + 1], a);
+          const bf16x8 k0 = fp8x8_to_bf16x8(kraw[u][w][0], kraw[u][w][1]);
+          const bf16x8 k1 = fp8x8_to_bf16x8(kraw[u][w][2], kraw[u][w][3]);
+#pragma unroll
+          for (int rb = 0; rb < NR; ++rb) {
+            a[rb] = mfma_16x16x32(k0, qB[rb][2 * w], a[rb]);
+            a[rb] = mfma_16x16x32(k1, qB[rb][2 * w + 1], a[rb]);
+          }
         }
       }
-      st[u] = a * c;
+#pragma unroll
+      for (int rb = 0; rb < NR; ++rb) st[rb][u] = a[rb] * c;
     }
     if constexpr (NB_EARLY < NB) {
 #pragma unroll
@@ -301,41 +325,51 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
     const bool tail = (T0 + CH - 1 > min_limit) || (T0 < max_lower);
     if (tail) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int tok0 = T0 + 32 * (u >> 1) + 8 * qd + 4 * (u & 1);
+      for (int rb = 0; rb < NR; ++rb)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) st[u][s] = (tok0 + s <= limit && tok0 + s >= lower) ? st[u][s] : kNegInf;
+        for (int u = 0; u < NU; ++u) {
+          const int tok0 = T0 + 32 * (u >> 1) + 8 * qd + 4 * (u & 1);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            st[rb][u][s] = (tok0 + s <= limit[rb] && tok0 + s >= lower[rb]) ? st[rb][u][s] : kNegInf;
+        }
+    }
+    float base[NR];
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb) {
+      float mloc = kNegInf;
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        mloc = fmaxf(fmaxf(mloc, fmaxf(st[rb][u][0], st[rb][u][1])), fmaxf(st[rb][u][2], st[rb][u][3]));
+      mloc = max_over_quads(mloc);
+      // Move the reference (and rescale what was accumulated) only where the new maximum is
+      // more than kLazyRescale above it; the first visible chunk of a row always moves it.
+      const bool move = mloc > mc[rb] + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float alpha = move ? ((mc[rb] == kNegInf) ? 0.f : fast_exp2(mc[rb] - mloc)) : 1.f;
+        mc[rb] = move ? mloc : mc[rb];
+        l[rb] *= alpha;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[rb][n] *= alpha;
       }
+      base[rb] = (mc[rb] == kNegInf) ? 0.f : mc[rb];
     }
-    float mloc = kNegInf;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) mloc = fmaxf(fmaxf(mloc, fmaxf(st[u][0], st[u][1])), fmaxf(st[u][2], st[u][3]));
-    mloc = max_over_quads(mloc);
-    // Move the reference (and rescale what was accumulated) only where the new maximum is
-    // more than kLazyRescale above it; the first visible chunk of a row always moves it.
-    const bool move = mloc > mc + kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(move) != 0) {
-      const float alpha = move ? ((mc == kNegInf) ? 0.f : fast_exp2(mc - mloc)) : 1.f;
-      mc = move ? mloc : mc;
-      l *= alpha;
-#pragma unroll
-      for (int n = 0; n < NB; ++n) acc[n] *= alpha;
-    }
-    const float base = (mc == kNegInf) ? 0.f : mc;
 
     // ---------------- P = 2^(t - mc), running sum, O^T += V^T . P^T (16x16x32 per d block, half)
     if (!tail) {
-      bf16x8 pB[NH];
+      bf16x8 pB[NR][NH];
 #pragma unroll
-      for (int h = 0; h < NH; ++h)
+      for (int rb = 0; rb < NR; ++rb)
 #pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          const float e0 = fast_exp2(st[2 * h + (t >> 2)][t & 3] - base);
-          const float e1 = fast_exp2(st[2 * h + (t >> 2)][(t & 3) + 1] - base);
-          l += e0 + e1;
-          pB[h][t] = (bf16)e0;
-          pB[h][t + 1] = (bf16)e1;
-        }
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int t = 0; t < 8; t += 2) {
+            const float e0 = fast_exp2(st[rb][2 * h + (t >> 2)][t & 3] - base[rb]);
+            const float e1 = fast_exp2(st[rb][2 * h + (t >> 2)][(t & 3) + 1] - base[rb]);
+            l[rb] += e0 + e1;
+            pB[rb][h][t] = (bf16)e0;
+            pB[rb][h][t + 1] = (bf16)e1;
+          }
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -343,19 +377,22 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
           bf16x8 va;
           if constexpr (KVT == KV_BF16) va = bitcast<bf16x8>(vraw[h][n]);
           else va = fp8x8_to_bf16x8(vraw[h][n][0], vraw[h][n][1]);
-          acc[n] = mfma_16x16x32(va, pB[h], acc[n]);
+#pragma unroll
+          for (int rb = 0; rb < NR; ++rb) acc[rb][n] = mfma_16x16x32(va, pB[rb][h], acc[rb][n]);
         }
     } else {
-      bf16x8 pB[NH], pL[NH];
+      bf16x8 pB[NR][NH], pL[NR][NH];
 #pragma unroll
-      for (int h = 0; h < NH; ++h)
+      for (int rb = 0; rb < NR; ++rb)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float e = fast_exp2(st[2 * h + (t >> 2)][t & 3] - base);
-          l += e;
-          pB[h][t] = (bf16)e;
-          pL[h][t] = (bf16)(e - (float)pB[h][t]);
-        }
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float e = fast_exp2(st[rb][2 * h + (t >> 2)][t & 3] - base[rb]);
+            l[rb] += e;
+            pB[rb][h][t] = (bf16)e;
+            pL[rb][h][t] = (bf16)(e - (float)pB[rb][h][t]);
+          }
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         // Keys past the end of the request are zeroed in V (their P is zero, but the slots may
@@ -368,43 +405,57 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
           else va = fp8x8_to_bf16x8(vraw[h][n][0], vraw[h][n][1]);
 #pragma unroll
           for (int t = 0; t < 8; ++t) va[t] = (t < vvalid) ? va[t] : (bf16)0.f;
-          acc[n] = mfma_16x16x32(va, pB[h], acc[n]);
-          acc[n] = mfma_16x16x32(va, pL[h], acc[n]);
+#pragma unroll
+          for (int rb = 0; rb < NR; ++rb) {
+            acc[rb][n] = mfma_16x16x32(va, pB[rb][h], acc[rb][n]);
+            acc[rb][n] = mfma_16x16x32(va, pL[rb][h], acc[rb][n]);
+          }
         }
       }
     }
   }
 
   // ---------------- combine the NW waves (fixed order) through LDS.
-  // lds layout: stats[2][NW][16] (reference maximum, sum) then O[NW][R][D].
+  // lds layout: stats[2][NW][16 NR] (reference maximum, sum) then O[NW][R][D].
+  constexpr int SR = 16 * NR;
   float* smax = lds;
-  float* ssum = lds + NW * 16;
-  float* so = lds + 2 * NW * 16;
-  const float l_row = sum_over_quads(l);
-  if (qd == 0) {
-    smax[wave * 16 + j] = mc;
-    ssum[wave * 16 + j] = l_row;
+  float* ssum = lds + NW * SR;
+  float* so = lds + 2 * NW * SR;
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb) {
+    const float l_row = sum_over_quads(l[rb]);
+    if (qd == 0) {
+      smax[wave * SR + 16 * rb + j] = mc[rb];
+      ssum[wave * SR + 16 * rb + j] = l_row;
+    }
   }
   __syncthreads();
-  float mx = kNegInf;
+  float mx[NR], ltot[NR];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, smax[w * 16 + j]);
-  const float mbase = (mx == kNegInf) ? 0.f : mx;
-  float ltot = 0.f;
+  for (int rb = 0; rb < NR; ++rb) {
+    const int r = 16 * rb + j;
+    mx[rb] = kNegInf;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const float mw = smax[w * 16 + j];
-    ltot += (mw == kNegInf) ? 0.f : ssum[w * 16 + j] * fast_exp2(mw - mbase);
-  }
-  const float own = (mc == kNegInf || ltot == 0.f) ? 0.f : fast_exp2(mc - mbase) * vscale / ltot;
-  if (j < R) {
-    float* dst = so + ((size_t)wave * R + j) * D;
+    for (int w = 0; w < NW; ++w) mx[rb] = fmaxf(mx[rb], smax[w * SR + r]);
+    const float mbase = (mx[rb] == kNegInf) ? 0.f : mx[rb];
+    ltot[rb] = 0.f;
 #pragma unroll
-    for (int n = 0; n < NB; ++n) *reinterpret_cast<f32x4*>(dst + 16 * n + 4 * qd) = acc[n] * own;
+    for (int w = 0; w < NW; ++w) {
+      const float mw = smax[w * SR + r];
+      ltot[rb] += (mw == kNegInf) ? 0.f : ssum[w * SR + r] * fast_exp2(mw - mbase);
+    }
+    const float own = (mc[rb] == kNegInf || ltot[rb] == 0.f) ? 0.f : fast_exp2(mc[rb] - mbase) * vscale / ltot[rb];
+    if (r < R) {
+      float* dst = so + ((size_t)wave * R + r) * D;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) *reinterpret_cast<f32x4*>(dst + 16 * n + 4 * qd) = acc[rb][n] * own;
+    }
   }
   __syncthreads();
 
-  const float row_lse = (ltot == 0.f) ? kNegInf : kLn2 * (mx + fast_log2(ltot));
+  float row_lse[NR];
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb) row_lse[rb] = (ltot[rb] == 0.f) ? kNegInf : kLn2 * (mx[rb] + fast_log2(ltot[rb]));
   if (direct) {
     for (int idx = tid; idx < R * (D / 4); idx += NW * 64) {
       const int r = idx / (D / 4), d4 = 4 * (idx - r * (D / 4));
@@ -414,14 +465,18 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
       const int i = r / p.g, h = kvh * p.g + r % p.g;
       *reinterpret_cast<bf16x4*>(p.out + ((size_t)(q0 + i) * p.Hq + h) * D + d4) = f32x4_to_bf16x4(o);
     }
-    if (p.lse && wave == 0 && qd == 0 && j < R) {
-      const int i = j / p.g, h = kvh * p.g + j % p.g;
-      p.lse[(size_t)(q0 + i) * p.Hq + h] = row_lse;
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb) {
+      const int r = 16 * rb + j;
+      if (p.lse && wave == 0 && qd == 0 && r < R) {
+        const int i = r / p.g, h = kvh * p.g + r % p.g;
+        p.lse[(size_t)(q0 + i) * p.Hq + h] = row_lse[rb];
+      }
     }
     return;
   }
   const size_t unit = (size_t)share * 2 + slot;
-  float* wo = p.ws_o + unit * 16 * D;
+  float* wo = p.ws_o + unit * p.max_rows * D;
   for (int idx = tid; idx < R * (D / 4); idx += NW * 64) {
     const int r = idx / (D / 4), d4 = 4 * (idx - r * (D / 4));
     f32x4 o = *reinterpret_cast<const f32x4*>(so + (0 * R + r) * D + d4);
@@ -429,7 +484,9 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
     for (int w = 1; w < NW; ++w) o += *reinterpret_cast<const f32x4*>(so + (w * R + r) * D + d4);
     *reinterpret_cast<f32x4*>(wo + r * D + d4) = o;
   }
-  if (wave == 0 && qd == 0 && j < R) p.ws_lse[unit * 16 + j] = row_lse;
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb)
+    if (wave == 0 && qd == 0 && 16 * rb + j < R) p.ws_lse[unit * p.max_rows + 16 * rb + j] = row_lse[rb];
 }
 
 // Exclusive prefix sums of count(b) over requests b < B into sp[0 .. B] (LDS); threads 0-255 scan
@@ -463,10 +520,10 @@ __device__ __forceinline__ void block_prefix(int B, Count count, int* sp, int* w
 // The partition kernel's body for a workgroup of NW waves: share g of the batch's chunks walks the
 // (request, kv head) pieces it covers. lds: the combine buffer of decode_piece
 // (decode_combine_floats), then sp[B + 1] and NW scratch ints.
-template <int D, int NW>
-constexpr int decode_combine_floats(int rows) { return 2 * NW * 16 + NW * rows * D; }
+template <int D, int NW, int NR = 1>
+constexpr int decode_combine_floats(int rows) { return 2 * NW * 16 * NR + NW * rows * D; }
 
-template <int D, int KVT, int NU, bool LONGV, int NW = 4>
+template <int D, int KVT, int NU, bool LONGV, int NW = 4, int NR = 1>
 __device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, int combine_floats, int g) {
   constexpr int CH = DecodeShape<NU>::CH;
   int* sp = reinterpret_cast<int*>(lds + combine_floats);
@@ -498,7 +555,7 @@ __device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, i
     // chunks are dealt to the waves round-robin over the whole share
     const int wave_first = (int)((wave - (pos - r0) % NW + NW) % NW);
     const int slot = (c0 == 0 && c1 == nb) ? -1 : (first ? 0 : 1);
-    decode_piece<D, KVT, NU, LONGV, NW>(p, b, kvh, c0, c1, wave_first, g, slot, lds);
+    decode_piece<D, KVT, NU, LONGV, NW, NR>(p, b, kvh, c0, c1, wave_first, g, slot, lds);
     pos += c1 - c0;
     first = false;
     if (c1 == nb && kvh == p.Hkv - 1) ++b;
@@ -520,7 +577,7 @@ __device__ __forceinline__ void merge_row(const PagedParams& p, int b, int kvh, 
   const int q0 = p.cu_seqlens_q ? p.cu_seqlens_q[b] : b;
   const int qlen = p.cu_seqlens_q ? (p.cu_seqlens_q[b + 1] - q0) : 1;
   const int R = qlen * p.g;
-  if (R > 16 || r >= R) return;                        // rows of another path, or no such row
+  if (R > p.max_rows || r >= R) return;                // rows of another path, or no such row
   const int tid = threadIdx.x;
   const int i = r / p.g, h = kvh * p.g + r % p.g;
   bf16* orow = p.out + ((size_t)(q0 + i) * p.Hq + h) * D;
@@ -556,8 +613,8 @@ __device__ __forceinline__ void merge_row(const PagedParams& p, int b, int kvh, 
         const int gk = g_lo + k;
         const bool has = k < ns && (FULL || share_start(gk, T, G) < share_start(gk + 1, T, G));
         const size_t piece = (size_t)gk * 2 + (k == 0 ? slot_lo : 0);
-        lk[u] = has ? p.ws_lse[piece * 16 + r] : kNegInf;
-        ok[u] = has ? *reinterpret_cast<const f32x4*>(p.ws_o + (piece * 16 + r) * D + 4 * dq)
+        lk[u] = has ? p.ws_lse[piece * p.max_rows + r] : kNegInf;
+        ok[u] = has ? *reinterpret_cast<const f32x4*>(p.ws_o + (piece * p.max_rows + r) * D + 4 * dq)
                     : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll

@@ -46,23 +46,24 @@ void prefill_pingpong_kernel(PrefillParams p) {
   prefill_pingpong_body<BN>(p, smem_raw, pair % HG, pair / HG, Z - 1 - t);
 }
 
-// Q-tiles of request b on the prefill path of a mixed batch (its rows do not fit the decode path).
-__device__ __forceinline__ int prefill_qtiles(const PrefillParams& p, int b, int tq) {
+// Q-tiles of request b on the prefill path of a mixed batch (its rows per KV head exceed
+// max_rows, the most the decode path takes).
+__device__ __forceinline__ int prefill_qtiles(const PrefillParams& p, int b, int tq, int max_rows) {
   const int lq = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
-  return (lq * p.g > 16) ? (lq + tq - 1) / tq : 0;
+  return (lq * p.g > max_rows) ? (lq + tq - 1) / tq : 0;
 }
 
 // Mixed varlen batch over a paged cache in one launch: workgroups [0, n_dec) are the decode
 // path's shares (memory-bound; dispatched first so that they run beside the prefill tiles), the
 // rest are prefill q-tiles (compute-bound), heaviest tile of each request first.
-template <int D, int BN, int KVT, int NU, bool LONGV>
+template <int D, int BN, int KVT, int NU, bool LONGV, int NR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D>(), prefill_waves_per_eu<D>())))
 void varlen_mixed_kernel(PrefillParams pp, PagedParams dp, int n_dec,
                                                            int combine_floats) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* lds = reinterpret_cast<float*>(smem_raw);
   if ((int)blockIdx.x < n_dec) {
-    decode_share<D, KVT, NU, LONGV>(dp, lds, combine_floats, blockIdx.x);
+    decode_share<D, KVT, NU, LONGV, 4, NR>(dp, lds, combine_floats, blockIdx.x);
     return;
   }
   using Loader = PagedLoader<D, BN, KVT == KV_FP8>;
@@ -71,7 +72,7 @@ void varlen_mixed_kernel(PrefillParams pp, PagedParams dp, int n_dec,
   const int hgrp = w % hg, t = w / hg;
   const int tq = 32 * (4 / pp.hpw);
   int* sp = reinterpret_cast<int*>(smem_raw + PrefillShape<D, BN>::LDS_BYTES);
-  block_prefix(pp.num_seqs, [&](int b) { return prefill_qtiles(pp, b, tq); }, sp, sp + pp.num_seqs + 1);
+  block_prefix(pp.num_seqs, [&](int b) { return prefill_qtiles(pp, b, tq, dp.max_rows); }, sp, sp + pp.num_seqs + 1);
   if (t >= sp[pp.num_seqs]) return;
   int lo = 0, hi = pp.num_seqs - 1;                    // the largest b with sp[b] <= t
   while (lo < hi) {
@@ -101,7 +102,7 @@ void varlen_mixed256_kernel(PrefillParams pp, PagedParams dp, int n_dec, int com
   const int hgrp = w % hg, t = w / hg;
   const int tq = 32 * (4 / pp.hpw);
   int* sp = reinterpret_cast<int*>(smem_raw + PingPong256Shape<KVT == KV_FP8>::LDS_BYTES);
-  block_prefix(pp.num_seqs, [&](int b) { return prefill_qtiles(pp, b, tq); }, sp, sp + pp.num_seqs + 1);
+  block_prefix(pp.num_seqs, [&](int b) { return prefill_qtiles(pp, b, tq, dp.max_rows); }, sp, sp + pp.num_seqs + 1);
   if (t >= sp[pp.num_seqs]) return;
   int lo = 0, hi = pp.num_seqs - 1;                    // the largest b with sp[b] <= t
   while (lo < hi) {
@@ -149,15 +150,22 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int max_seqlen, 
   return hipErrorInvalidValue;
 }
 
+// Rows per (request, kv head) that the decode role of the mixed kernel takes at most: 32 with
+// head_dim 128 (two 16-row blocks; their combine buffer fits beside the prefill tiles), 16 with
+// head_dim 256 (8 waves' combine buffer of 32 rows would not fit the LDS).
+template <int D>
+constexpr int mixed_max_rows() { return D == 128 ? 32 : 16; }
+
 // Dynamic LDS of the mixed kernel: the larger of the prefill tile buffers and the decode combine
-// buffer of its NW waves, then num_seqs + 1 + NW ints (prefix sums and per-wave scratch). Head_dim
-// 128: 4 waves and the tiles of prefill_core.h; head_dim 256: 8 waves and the tiles of
-// prefill_pp256.h (the same for both cache dtypes).
+// buffer of its NW waves (for the most rows it takes), then num_seqs + 1 + NW ints (prefix sums and
+// per-wave scratch). Head_dim 128: 4 waves and the tiles of prefill_core.h; head_dim 256: 8 waves
+// and the tiles of prefill_pp256.h (the same for both cache dtypes).
 template <int D>
 static size_t mixed_lds_bytes(int num_seqs) {
   constexpr int NW = D == 256 ? 8 : 4;
+  constexpr int NR = mixed_max_rows<D>() / 16;
   const size_t tiles = D == 256 ? (size_t)PingPong256Shape<false>::LDS_BYTES : (size_t)PrefillShape<D, 64>::LDS_BYTES;
-  const size_t combine = (size_t)decode_combine_floats<D, NW>(16) * sizeof(float);
+  const size_t combine = (size_t)decode_combine_floats<D, NW, NR>(16 * NR) * sizeof(float);
   return std::max(tiles, combine) + ((size_t)num_seqs + 1 + NW) * sizeof(int);
 }
 
@@ -173,8 +181,10 @@ int mixed_max_seqs(int head_dim) {
   return head_dim == 128 ? mixed_max_seqs_t<128>() : mixed_max_seqs_t<256>();
 }
 
-template <int D, int BN, int KVT, int NU, bool LONGV>
+// NR: 16-row blocks of the decode role (dp.max_rows / 16).
+template <int D, int BN, int KVT, int NU, bool LONGV, int NR>
 static hipError_t launch_mixed_t(const PrefillParams& pp, const PagedParams& dp, int total_q, hipStream_t stream) {
+  static_assert(16 * NR <= mixed_max_rows<D>(), "the decode role's rows fit its combine buffer");
   const int tq = 32 * (4 / pp.hpw);
   // upper bound on prefill q-tiles: every request adds at most one partial tile
   const long long n_pre = (long long)pp.Hkv * (pp.g / pp.hpw) * ((total_q + tq - 1) / tq + pp.num_seqs);
@@ -184,7 +194,7 @@ static hipError_t launch_mixed_t(const PrefillParams& pp, const PagedParams& dp,
   static std::atomic<bool> done[kMaxDevices];
   const void* fn;
   if constexpr (D == 256) fn = reinterpret_cast<const void*>(&varlen_mixed256_kernel<KVT, NU, LONGV>);
-  else fn = reinterpret_cast<const void*>(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV>);
+  else fn = reinterpret_cast<const void*>(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV, NR>);
   hipError_t e = ensure_dynamic_lds(fn, done, (int)mixed_lds_bytes<D>(mixed_max_seqs_t<D>()));
   if (e != hipSuccess) return e;
   e = ensure_merge_attrs(D, NU);
@@ -193,19 +203,30 @@ static hipError_t launch_mixed_t(const PrefillParams& pp, const PagedParams& dp,
   const size_t lds = mixed_lds_bytes<D>(pp.num_seqs);
   if constexpr (D == 256) {
     e = launch_kernel(&varlen_mixed256_kernel<KVT, NU, LONGV>, grid, dim3(512), lds, stream, pp, dp, n_dec,
-                      decode_combine_floats<256, 8>(16));
+                      decode_combine_floats<256, 8, NR>(16 * NR));
   } else {
-    e = launch_kernel(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV>, grid, dim3(256), lds, stream, pp, dp, n_dec,
-                      decode_combine_floats<D, 4>(16));
+    e = launch_kernel(&varlen_mixed_kernel<D, BN, KVT, NU, LONGV, NR>, grid, dim3(256), lds, stream, pp, dp, n_dec,
+                      decode_combine_floats<D, 4, NR>(16 * NR));
   }
   if (e != hipSuccess) return e;
-  return launch_decode_merge(dp, D, NU, 16, stream);
+  return launch_decode_merge(dp, D, NU, dp.max_rows, stream);
+}
+
+template <int D, int BN, int KVT, int NU, int NR>
+static hipError_t launch_mixed_nr(const PrefillParams& pp, const PagedParams& dp, int total_q, hipStream_t stream) {
+  return dp.bs > 32 ? launch_mixed_t<D, BN, KVT, NU, true, NR>(pp, dp, total_q, stream)
+                    : launch_mixed_t<D, BN, KVT, NU, false, NR>(pp, dp, total_q, stream);
 }
 
 template <int D, int BN, int KVT, int NU>
 static hipError_t launch_mixed_bs(const PrefillParams& pp, const PagedParams& dp, int total_q, hipStream_t stream) {
-  return dp.bs > 32 ? launch_mixed_t<D, BN, KVT, NU, true>(pp, dp, total_q, stream)
-                    : launch_mixed_t<D, BN, KVT, NU, false>(pp, dp, total_q, stream);
+  // two row blocks take 32-token chunks (NU = 2), so that their registers fit beside the prefill
+  // role's two waves per SIMD
+  if constexpr (mixed_max_rows<D>() >= 32) {
+    if (dp.max_rows > 16) return launch_mixed_nr<D, BN, KVT, 2, 2>(pp, dp, total_q, stream);
+  }
+  if (dp.max_rows != 16) return hipErrorInvalidValue;
+  return launch_mixed_nr<D, BN, KVT, NU, 1>(pp, dp, total_q, stream);
 }
 
 hipError_t launch_mixed(const PrefillParams& pp, const PagedParams& dp, int head_dim, int kv_type, int total_q,

@@ -241,9 +241,9 @@ def mixed_section(lib, case, steps, warmup):
 
 def multi_token_section(lib, case, steps, warmup, q_len=4):
     """Speculative-verification decode on the batch-32 cache: each request's last q_len cached
-    tokens are new query rows, through the mixed varlen call (up to 16 rows per KV head, g * q_len,
-    take the split-KV decode path; more take the prefill tiles). Algorithmic bytes: the K/V bytes,
-    as for the decode."""
+    tokens are new query rows, through the mixed varlen call (at head_dim 128 up to 32 rows per KV
+    head, g * q_len, take the split-KV decode path, in one or two 16-row blocks; more take the
+    prefill tiles). Algorithmic bytes: the K/V bytes, as for the decode."""
     import torch
     from attention_gqa_flash_02_amd import workmodel
     dev = case.q.device
@@ -264,7 +264,8 @@ def multi_token_section(lib, case, steps, warmup, q_len=4):
     gbs = kv_bytes / kern / 1e6
     log(f"[bench] multi-token decode q_len={q_len}: call mean={kern * 1e3:.1f} us -> {gbs:.0f} GB/s")
     rows = hq // case.num_kv_heads * q_len
-    path = "split-KV decode path" if rows <= 16 else "prefill tiles"
+    path = ("split-KV decode path" if rows <= 16 else
+            "split-KV decode path, two 16-row blocks" if rows <= 32 and d == 128 else "prefill tiles")
     return {"workload": f"batch-32 paged decode cache (32/8 heads, D 128, bf16, 16-token pages), {q_len} new "
                         f"query rows per request ({rows} rows per KV head: {path})",
             "q_len": q_len, "kv_bytes": kv_bytes, "ms": kern, "wall_ms": wall, "gbs": gbs, "timing": info,

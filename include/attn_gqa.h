@@ -237,10 +237,16 @@ attn_status attn_decode_paged_noalloc(const void* q, const void* k_cache, const 
  * own new tokens being the last Lq of them (a prefill chunk over a cached
  * prefix, or a decode token). Requests whose Lq * (num_q_heads/num_kv_heads)
  * is at most 16 run on the split-KV decode path (num_splits partitions, as in
- * attn_decode_paged); the others run on the tiled prefill path.
+ * attn_decode_paged); with head_dim 128 so do requests of up to 32 such rows
+ * when max_q_len * (num_q_heads/num_kv_heads) exceeds 16 (several new tokens
+ * per request, as in speculative verification); the others run on the tiled
+ * prefill path. max_q_len is the largest Lq (a smaller value is not an error:
+ * it only sends requests of 17-32 rows to the prefill path).
  *   q, out [total_q, num_q_heads, head_dim] bf16; lse [total_q, num_q_heads] fp32 or NULL
  *   causal: 0 or 1 (bottom-right aligned)
- *   workspace: >= attn_varlen_workspace_bytes(...) bytes of device scratch.
+ *   workspace: >= attn_varlen_workspace_bytes(...) bytes of device scratch:
+ *     per partition two partial results of 32 rows (head_dim 128) or 16 rows
+ *     (head_dim 256) x (head_dim + 1) floats, then num_seqs + 1 int32.
  * With head_dim 256, num_seqs above 7927 returns ATTN_ERR_UNSUPPORTED (the
  * kernel keeps per-request offsets in LDS beside its 129 KB of tiles or
  * partial results).

@@ -196,7 +196,8 @@ def test_varlen_group_sizes(gpu, hq, hkv):
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (16, 4), (16, 2)])
 def test_varlen_multi_token_decode(gpu, hq, hkv):
     """Speculative verification: 2-8 new query rows per request over a long cache; rows that fit
-    16 per KV head go through the split-KV decode path, the others through the prefill path."""
+    32 per KV head (head_dim 128) go through the split-KV decode path, in one or two 16-row blocks,
+    the others through the prefill path."""
     q_lens = [2, 3, 4, 5, 6, 7, 8, 1]
     kv_lens = [900, 2000, 64, 17, 3000, 33, 1500, 700]
     gen = torch.Generator().manual_seed(300 + hq + hkv)

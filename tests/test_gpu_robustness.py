@@ -82,9 +82,10 @@ def test_nan_poison_decode(gpu, kv_format, d, bs):
 @pytest.mark.parametrize("d,bs", [(128, 16), (256, 16), (256, 64)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_nan_poison_mixed(gpu, kv_format, d, bs, causal):
-    """Decode rows and paged prefill chunks (over prefixes and without) in one call."""
-    q_lens = [1, 3, 37, 64, 130, 1, 70]
-    kv_lens = [5, 300, 37, 64 + 500, 130 + 33, 2000, 70 + 1]
+    """Decode rows (at head_dim 128 also a request of 24 rows per KV head: two 16-row blocks) and
+    paged prefill chunks (over prefixes and without) in one call."""
+    q_lens = [1, 3, 37, 64, 130, 1, 70, 6]
+    kv_lens = [5, 300, 37, 64 + 500, 130 + 33, 2000, 70 + 1, 6 + 251]
     gen = torch.Generator().manual_seed(820 + d + bs)
     case = synth.make_paged(820 + d + bs, kv_lens, q_lens, 8, 2, d, bs, kv_format=kv_format, causal=causal,
                             poison=NAN, lengths_drawn=gen)
