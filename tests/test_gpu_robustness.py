@@ -198,6 +198,10 @@ def test_mixed_and_decode_repeat_bitwise(gpu):
     _same_every_time(lambda: _varlen(case, 0))
     dec = _to(synth.config_case("c2", shrink=4), gpu)
     _same_every_time(lambda: _decode(dec, 0))
+    # several new tokens per request at group 4: the decode role's two 16-row blocks
+    gen = torch.Generator().manual_seed(950)
+    mt = _to(synth.make_paged(950, [900, 2000, 64, 1500], [6, 8, 5, 1], 16, 4, 128, 16, lengths_drawn=gen), gpu)
+    _same_every_time(lambda: _varlen(mt, 0))
 
 
 # ---------------------------------------------------------------------------------------------
