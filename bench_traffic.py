@@ -1,6 +1,7 @@
-"""HBM traffic and matrix-core use per call of the attention kernels, from hardware counters.
+"""HBM traffic and matrix-core use per call of the attention kernels, from hardware counters,
+and the board's power and clocks while a workload runs.
 
-Three sub-commands:
+Four sub-commands:
 
   python bench_traffic.py copy
       Launches a plain elementwise copy (fp32, 1 GiB read + 1 GiB written, 8 times) and nothing
@@ -27,6 +28,14 @@ Three sub-commands:
           rocprofv3 derives as MfmaUtil;
         * achieved MFMA FLOP per busy cycle against the chip's dense peak per cycle (256 compute
           units x 4096 bf16 FLOP, x 8192 for fp8).
+
+  python bench_traffic.py power [--seconds S]
+      Runs the 4 x 8192 causal prefill (bf16, then fp8 e4m3fn) back to back for S seconds each,
+      with an idle second before each, while a thread reads the GPU's metrics table through amdsmi
+      every 20 ms. Prints, per phase (the first half second of each left out), the calls per second,
+      the median board power and graphics clock (the mean over the 8 XCDs), the power cap, and the
+      fraction of the phase's time that the firmware spent holding power under the cap (the change
+      of ppt_residency_acc over the change of accumulation_counter).
 """
 
 import argparse
@@ -52,6 +61,75 @@ def run_copy():
     torch.cuda.synchronize()
     print(json.dumps({"kernel": "elementwise add (copy)", "bytes_read": 4 * COPY_ELEMS,
                       "bytes_written": 4 * COPY_ELEMS, "dispatches": COPY_REPS}))
+
+
+def run_power(seconds):
+    import threading
+    import time
+
+    import amdsmi
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import attention_gqa_flash_02_amd as lib
+    import synth
+
+    amdsmi.amdsmi_init()
+    handle = amdsmi.amdsmi_get_processor_handles()[0]
+    cap_w = amdsmi.amdsmi_get_power_cap_info(handle).get("power_cap", 0) / 1e6
+    samples, done = [], threading.Event()
+
+    def sample():
+        while not done.is_set():
+            samples.append((time.time(), amdsmi.amdsmi_get_gpu_metrics_info(handle)))
+            time.sleep(0.02)
+
+    dev = torch.device("cuda:0")
+    bf = synth.config_case("c3", device=dev)
+    f8 = synth.make_prefill_fp8(3, [8192] * 4, 32, 8, 128, device=dev)
+    out, lse = lib.attn_prefill_varlen(bf.q, bf.k, bf.v, bf.cu_seqlens, True, bf.scale, max_seqlen=8192)
+    out8, lse8 = lib.attn_prefill_varlen_fp8(f8.q, f8.k, f8.v, f8.q_scale, f8.k_scale, f8.v_scale, f8.cu_seqlens,
+                                             True, f8.scale, max_seqlen=8192)
+    torch.cuda.synchronize()
+    calls = {
+        "prefill bf16 4x8192": lambda: lib.attn_prefill_varlen(bf.q, bf.k, bf.v, bf.cu_seqlens, True, bf.scale,
+                                                               out=out, lse=lse, max_seqlen=8192),
+        "prefill fp8 4x8192": lambda: lib.attn_prefill_varlen_fp8(f8.q, f8.k, f8.v, f8.q_scale, f8.k_scale,
+                                                                  f8.v_scale, f8.cu_seqlens, True, f8.scale,
+                                                                  out=out8, lse=lse8, max_seqlen=8192),
+    }
+    thread = threading.Thread(target=sample, daemon=True)
+    thread.start()
+    phases = []
+    for name, call in calls.items():
+        t0 = time.time()
+        time.sleep(1.0)
+        phases.append(("idle", t0, time.time(), 0))
+        t0, n = time.time(), 0
+        while time.time() - t0 < seconds:
+            for _ in range(10):
+                call()
+            n += 10
+            torch.cuda.synchronize()
+        phases.append((name, t0, time.time(), n))
+    done.set()
+    thread.join()
+
+    def num(x):
+        return isinstance(x, (int, float)) and not isinstance(x, bool)
+
+    for name, t0, t1, n in phases:
+        ms = [m for t, m in samples if t0 + 0.5 <= t <= t1]
+        if len(ms) < 2:
+            continue
+        clocks = [statistics.mean(c for c in m["current_gfxclks"] if num(c) and c < 65535) for m in ms]
+        power = [m["current_socket_power"] for m in ms if num(m.get("current_socket_power"))]
+        acc = ms[-1]["accumulation_counter"] - ms[0]["accumulation_counter"]
+        ppt = (ms[-1]["ppt_residency_acc"] - ms[0]["ppt_residency_acc"]) / acc if acc > 0 else None
+        print(json.dumps({"phase": name, "calls_per_s": round(n / (t1 - t0), 1) if n else 0,
+                          "samples": len(ms), "power_w": statistics.median(power) if power else None,
+                          "power_cap_w": cap_w, "gfxclk_mhz": round(statistics.median(clocks), 1),
+                          "ppt_limit_frac": round(ppt, 3) if ppt is not None else None}))
 
 
 def read_counter(path, counter):
@@ -158,6 +236,8 @@ def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     sub.add_parser("copy")
+    pw = sub.add_parser("power")
+    pw.add_argument("--seconds", type=float, default=4.0)
     cnt = sub.add_parser("counters")
     cnt.add_argument("csv")
     cnt.add_argument("--kernel", default=None)
@@ -167,6 +247,8 @@ def main():
     a = ap.parse_args()
     if a.cmd == "copy":
         run_copy()
+    elif a.cmd == "power":
+        run_power(a.seconds)
     elif a.cmd == "counters":
         counters(a)
     else:
