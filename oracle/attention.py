@@ -9,7 +9,7 @@ are set to -inf, the softmax subtracts the row maximum before exponentiating,
 and the per-row statistic written beside O is the natural-log
 log-sum-exp of the scaled scores.
 
-Readings where the pages say nothing (each is listed in the design doc):
+Readings where the pages say nothing:
   * scores are multiplied by a caller-supplied ``scale`` (1/sqrt(D) in every
     workload);
   * GQA head mapping is contiguous: query head h reads KV head h // g with

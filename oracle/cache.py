@@ -12,7 +12,7 @@ attention calls do). Token t lands in physical block block_table[b, t // bs], sl
 K row [block, h, slot, :], V column [block, h, :, slot] (the layouts the attention oracle
 gathers from). Nothing else changes.
 
-Readings (listed in the design doc): a bf16 cache stores the bf16 bits unchanged; an fp8 cache
+Readings where the pages say nothing: a bf16 cache stores the bf16 bits unchanged; an fp8 cache
 stores e4m3fn(x / scale[h]) -- the quotient computed in fp32, the precision the kernel divides
 in, then rounded to the nearest code (ties to even) and saturated at 448 (``encode_e4m3fn``).
 """
