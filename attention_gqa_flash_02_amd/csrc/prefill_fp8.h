@@ -280,15 +280,16 @@ __device__ __forceinline__ void prefill_fp8_body(const PrefillFp8Params& p, unsi
     // every P stays at most 2^8, inside e4m3's range; else the tile is redone below, where the
     // reference moves).
     if (!split && __builtin_amdgcn_ballot_w64(mc == kNegInf) == 0) {
-      float tsum = 0.f;
+      float tsum;
 #pragma unroll
       for (int w = 0; w < 2 * NKB * 2; ++w) {
         const int kb = w / 4, r = 4 * (w % 4);
         float e[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) e[q] = fast_exp2(st[kb][r + q]);
+        const float s4 = (e[0] + e[1]) + (e[2] + e[3]);   // summed before the packing takes a's register
+        tsum = (w == 0) ? s4 : tsum + s4;
         pB[w] = pack_fp8x4(e[0], e[1], e[2], e[3]);
-        tsum += (e[0] + e[1]) + (e[2] + e[3]);
       }
       if (__builtin_amdgcn_ballot_w64(!(tsum <= 256.f)) == 0) {
         l += tsum;

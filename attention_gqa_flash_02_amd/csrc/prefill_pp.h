@@ -288,7 +288,7 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
       // first tile, the maximum is taken on the first and the masked tiles only.
       if (!edge && __builtin_amdgcn_ballot_w64(mc == kNegInf) == 0) {
         const float nbase = -mc;
-        float ts[2] = {0.f, 0.f};
+        float ts[2];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -302,7 +302,8 @@ __device__ __forceinline__ void prefill_pingpong_body(const PrefillParams& p, un
               pB[kb][t][q] = pe[0];
               pB[kb][t][q + 1] = pe[1];
             }
-            ts[t] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+            const float s8 = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+            ts[t] = (kb == 0) ? s8 : ts[t] + s8;
           }
         const float tsum = ts[0] + ts[1];
         if (__builtin_amdgcn_ballot_w64(!(tsum <= kFastLimit)) == 0) {
