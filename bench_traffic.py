@@ -1,7 +1,7 @@
 """HBM traffic and matrix-core use per call of the attention kernels, from hardware counters,
 and the board's power and clocks while a workload runs.
 
-Four sub-commands:
+Five sub-commands:
 
   python bench_traffic.py copy
       Launches a plain elementwise copy (fp32, 1 GiB read + 1 GiB written, 8 times) and nothing
@@ -36,6 +36,13 @@ Four sub-commands:
       the median board power and graphics clock (the mean over the 8 XCDs), the power cap, and the
       fraction of the phase's time that the firmware spent holding power under the cap (the change
       of ppt_residency_acc over the change of accumulation_counter).
+
+  python bench_traffic.py stream
+      Times plain streaming reductions and a copy through torch over 2 GiB tensors (sum, max and
+      a copy of bf16 and fp32 data, 4 rotating copies so nothing is served from the 256 MB
+      last-level cache), as a practical reference for what one MI355X reads per second outside
+      this library; prints the bytes moved per second of each, from HIP events (median of 30
+      calls after 20 warm-up calls).
 """
 
 import argparse
@@ -130,6 +137,39 @@ def run_power(seconds):
                           "samples": len(ms), "power_w": statistics.median(power) if power else None,
                           "power_cap_w": cap_w, "gfxclk_mhz": round(statistics.median(clocks), 1),
                           "ppt_limit_frac": round(ppt, 3) if ppt is not None else None}))
+
+
+def run_stream():
+    import torch
+
+    dev = torch.device("cuda:0")
+    nbytes = 2 << 30
+    results = []
+    for dtype in (torch.bfloat16, torch.float32):
+        n = nbytes // torch.tensor([], dtype=dtype).element_size()
+        xs = [torch.ones(n, dtype=dtype, device=dev) for _ in range(4)]
+        out = torch.empty_like(xs[0])
+        ops = {"sum": (lambda x: x.sum(), nbytes), "max": (lambda x: x.max(), nbytes),
+               "copy": (lambda x: out.copy_(x), 2 * nbytes)}
+        for name, (op, moved) in ops.items():
+            for i in range(20):
+                op(xs[i % 4])
+            torch.cuda.synchronize()
+            ms = []
+            for i in range(30):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                op(xs[i % 4])
+                e1.record()
+                e1.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            med = statistics.median(ms)
+            results.append({"op": f"{name} {str(dtype).replace('torch.', '')}", "bytes_per_call": moved,
+                            "ms_median": round(med, 4), "ms_min": round(min(ms), 4),
+                            "gb_per_s_median": round(moved / med / 1e6, 1),
+                            "gb_per_s_best": round(moved / min(ms) / 1e6, 1)})
+            print(json.dumps(results[-1]), flush=True)
+        del xs, out
 
 
 def read_counter(path, counter):
@@ -236,6 +276,7 @@ def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     sub.add_parser("copy")
+    sub.add_parser("stream")
     pw = sub.add_parser("power")
     pw.add_argument("--seconds", type=float, default=4.0)
     cnt = sub.add_parser("counters")
@@ -249,6 +290,8 @@ def main():
         run_copy()
     elif a.cmd == "power":
         run_power(a.seconds)
+    elif a.cmd == "stream":
+        run_stream()
     elif a.cmd == "counters":
         counters(a)
     else:
