@@ -63,7 +63,8 @@ struct PagedParams {
   float* lse;                  // [Tq, Hq] or nullptr
   float* ws_o;                 // [G, 2, max_rows, D] partial outputs (normalised)
   float* ws_lse;               // [G, 2, max_rows] partial natural-log LSEs
-  int32_t* ws_prefix;          // [B + 1] chunk-count prefix sums, written by workgroup 0
+  int32_t* ws_prefix;          // [B + 1] prefix sums of the planned lengths (decode_plan_len),
+                               // written by workgroup 0
   float scale;
   int num_seqs, Hq, Hkv, g, bs, max_blocks, num_wg, causal;
   int max_rows;                // 16 or 32: most query rows of one (request, kv head) on this path,
@@ -90,14 +91,29 @@ __device__ __forceinline__ int decode_chunks(const PagedParams& p, int b) {
   return (len + CH - 1) / CH - decode_key_begin(p, len, qlen) / CH;
 }
 
-// First chunk of workgroup g's share of T chunks: shares are whole groups of 4 chunks,
+// Share planning. The batch's work is the request-major list of (request, kv head) units. In
+// the plan a unit of 0 < nb < kPieceCostUnits chunks is kPieceCost + nb long: its first
+// kPieceCost places stand for the fixed cost of starting a piece of it (the cross-wave combine
+// and the block-table and K/V latency before its first chunk: about 1.9 us, 1.5 chunks of 64
+// tokens, measured as the extra time of a share per extra piece), and the next nb are its chunks.
+// Shares are equal parts of the planned list, so a share that crosses more short units streams
+// fewer chunks. Longer units span many shares, where the few extra pieces matter less than
+// keeping the list's length (shares are cut in groups of 4 places, and a share's time follows its
+// groups: one extra group in a share of 8 is an eighth longer).
+constexpr int kPieceCost = 2;
+constexpr int kPieceCostUnits = 256;
+__device__ __forceinline__ int decode_plan_len(int nb) {
+  return (nb > 0 && nb < kPieceCostUnits) ? nb + kPieceCost : nb;
+}
+
+// First place of workgroup g's share of T planned places: shares are whole groups of 4 places,
 // as equal as possible.
 __device__ __forceinline__ long long share_start(long long g, long long T, int G) {
   const long long quads = (T + 3) / 4;
   const long long s = 4 * ((g * quads) / G);
   return s < T ? s : T;
 }
-// The workgroup whose share holds chunk x (0 <= x < T).
+// The workgroup whose share holds place x (0 <= x < T).
 __device__ __forceinline__ int share_of(long long x, long long T, int G) {
   const long long quads = (T + 3) / 4;
   return (int)(((x / 4 + 1) * G + quads - 1) / quads - 1);
@@ -110,16 +126,18 @@ struct DecodeShape {
   static constexpr int NH = NU / 2;    // 32-token halves per chunk
 };
 
-// One piece of a (request, kv head) unit: chunks [c0, c1) of the unit; the waves start at chunk
-// c0 + first[w] and step by NW chunks. Rows of a request on this path: r -> (new token r / g,
-// query head kvh*g + r % g). slot < 0: the piece is the whole unit and is written to out/lse;
-// else it is written to partial slot `slot` of the workspace. LONGV: V page rows are longer than
-// one 32-token half (block size > 32), which decides how the V loads are issued. NR: blocks of 16
+// One piece of a (request, kv head) unit: places [u0, u1) of the unit's ul planned places (see
+// the share planning above), i.e. its chunks [c0, c1); the waves start at chunk c0 + first[w] and
+// step by NW chunks. Returns the number of chunks (0: the places hold none, and nothing is done).
+// Rows of a request on this path: r -> (new token r / g, query head kvh*g + r % g). A piece that
+// is the whole unit is written to out/lse; else it goes to partial slot 0 (the share's first
+// piece with a chunk, `first`) or 1 of the workspace. LONGV: V page rows are longer than one
+// 32-token half (block size > 32), which decides how the V loads are issued. NR: blocks of 16
 // rows (1, or 2 for up to 32 rows: several new tokens of a request at group size 4 and up); each K
 // and V operand is loaded and converted once and feeds the MFMAs of every row block.
 template <int D, int KVT, int NU, bool LONGV, int NW, int NR = 1>
-__device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kvh, int c0, int c1, int wave_first,
-                                             int share, int slot, float* lds) {
+__device__ __forceinline__ int decode_piece(const PagedParams& p, int b, int kvh, int u0, int u1, int ul,
+                                            int wave_first, int share, bool first, float* lds) {
   constexpr int CH = DecodeShape<NU>::CH;
   constexpr int NH = DecodeShape<NU>::NH;
   constexpr int KK = D / 32;        // QK MFMAs per 16-key sub-tile
@@ -135,8 +153,12 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
   const int q0 = p.cu_seqlens_q ? p.cu_seqlens_q[b] : b;
   const int qlen = p.cu_seqlens_q ? (p.cu_seqlens_q[b + 1] - q0) : 1;
   const int R = qlen * p.g;
-  const bool direct = slot < 0;
   const int kc0 = decode_key_begin(p, len, qlen) / CH;   // chunk c of the unit is key chunk kc0 + c
+  const int nb = (len + CH - 1) / CH - kc0;              // the unit's chunks (decode_chunks)
+  const int cost = ul - nb;                              // its planned places before them
+  const int c0 = max(0, u0 - cost), c1 = max(0, u1 - cost);   // empty: see below
+  const bool direct = c0 == 0 && c1 == nb;
+  const int slot = direct ? -1 : (first ? 0 : 1);
   const int t_end = min(len, (kc0 + c1) * CH);
 
   float kscale = 1.f, vscale = 1.f;
@@ -176,6 +198,9 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
   for (int rb = 0; rb < NR; ++rb)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(qB[rb][kk]));
+  // A piece whose places hold no chunk returns here, after the Q loads (which do not wait for the
+  // request's length, so they are in flight together with it).
+  if (c1 <= c0) return 0;
 
   // Running statistics of row j, in the base-2 exponent domain t = c * s: mc is a reference
   // maximum (the same in all four quads), l this lane's share of sum 2^(t - mc). The reference
@@ -473,7 +498,7 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
         p.lse[(size_t)(q0 + i) * p.Hq + h] = row_lse[rb];
       }
     }
-    return;
+    return c1 - c0;
   }
   const size_t unit = (size_t)share * 2 + slot;
   float* wo = p.ws_o + unit * p.max_rows * D;
@@ -487,6 +512,7 @@ __device__ __forceinline__ void decode_piece(const PagedParams& p, int b, int kv
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb)
     if (wave == 0 && qd == 0 && 16 * rb + j < R) p.ws_lse[unit * p.max_rows + 16 * rb + j] = row_lse[rb];
+  return c1 - c0;
 }
 
 // Exclusive prefix sums of count(b) over requests b < B into sp[0 .. B] (LDS); threads 0-255 scan
@@ -528,14 +554,14 @@ __device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, i
   constexpr int CH = DecodeShape<NU>::CH;
   int* sp = reinterpret_cast<int*>(lds + combine_floats);
   int* wave_tot = sp + p.num_seqs + 1;
-  block_prefix(p.num_seqs, [&](int b) { return decode_chunks<CH>(p, b); }, sp, wave_tot);
+  block_prefix(p.num_seqs, [&](int b) { return decode_plan_len(decode_chunks<CH>(p, b)); }, sp, wave_tot);
   const int B = p.num_seqs, G = p.num_wg;
   if (g == 0)
     for (int b = threadIdx.x; b <= B; b += NW * 64) p.ws_prefix[b] = sp[b];
   const long long T = (long long)p.Hkv * sp[B];
   const long long r0 = share_start(g, T, G), r1 = share_start(g + 1, T, G);
   if (r0 >= r1) return;
-  // request holding chunk r0: the largest b < B with Hkv * sp[b] <= r0
+  // request holding place r0: the largest b < B with Hkv * sp[b] <= r0
   int lo = 0, hi = B - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -543,22 +569,23 @@ __device__ __forceinline__ void decode_share(const PagedParams& p, float* lds, i
   }
   int b = lo;
   long long pos = r0;
+  int dealt = 0;                       // chunks of the share so far
   bool first = true;
   const int wave = threadIdx.x >> 6;
   while (pos < r1) {
-    const int nb = sp[b + 1] - sp[b];
-    if (nb == 0) { ++b; continue; }
+    const int ul = sp[b + 1] - sp[b];  // planned length of each unit of request b
+    if (ul == 0) { ++b; continue; }
     const long long base = (long long)p.Hkv * sp[b];
-    const int kvh = (int)((pos - base) / nb);
-    const int c0 = (int)(pos - base - (long long)kvh * nb);
-    const int c1 = (int)min((long long)nb, c0 + (r1 - pos));
+    const int kvh = (int)((pos - base) / ul);
+    const int u0 = (int)(pos - base - (long long)kvh * ul);        // places of the unit in the share:
+    const int u1 = (int)min((long long)ul, u0 + (r1 - pos));      // [u0, u1)
     // chunks are dealt to the waves round-robin over the whole share
-    const int wave_first = (int)((wave - (pos - r0) % NW + NW) % NW);
-    const int slot = (c0 == 0 && c1 == nb) ? -1 : (first ? 0 : 1);
-    decode_piece<D, KVT, NU, LONGV, NW, NR>(p, b, kvh, c0, c1, wave_first, g, slot, lds);
-    pos += c1 - c0;
-    first = false;
-    if (c1 == nb && kvh == p.Hkv - 1) ++b;
+    const int wave_first = ((wave - dealt) % NW + NW) % NW;
+    const int n = decode_piece<D, KVT, NU, LONGV, NW, NR>(p, b, kvh, u0, u1, ul, wave_first, g, first, lds);
+    dealt += n;
+    first = first && n == 0;
+    pos += u1 - u0;
+    if (u1 == ul && kvh == p.Hkv - 1) ++b;
   }
 }
 
@@ -581,7 +608,8 @@ __device__ __forceinline__ void merge_row(const PagedParams& p, int b, int kvh, 
   const int tid = threadIdx.x;
   const int i = r / p.g, h = kvh * p.g + r % p.g;
   bf16* orow = p.out + ((size_t)(q0 + i) * p.Hq + h) * D;
-  const int nb = p.ws_prefix[b + 1] - p.ws_prefix[b];
+  const int ul = p.ws_prefix[b + 1] - p.ws_prefix[b];  // planned length of the unit
+  const int nb = decode_chunks<CH>(p, b);
   if (nb == 0) {                                       // no key at all
     if (tid < DQ) *reinterpret_cast<bf16x4*>(orow + 4 * tid) = bf16x4{};
     if (p.lse && tid == 0) p.lse[(size_t)(q0 + i) * p.Hq + h] = kNegInf;
@@ -589,18 +617,20 @@ __device__ __forceinline__ void merge_row(const PagedParams& p, int b, int kvh, 
   }
   const int G = p.num_wg;
   const long long T = (long long)p.Hkv * p.ws_prefix[p.num_seqs];
-  const long long start = (long long)p.Hkv * p.ws_prefix[b] + (long long)kvh * nb;
+  const long long ustart = (long long)p.Hkv * p.ws_prefix[b] + (long long)kvh * ul;   // the unit's places
+  const long long start = ustart + (ul - nb);          // its first chunk
   const int g_lo = share_of(start, T, G), g_hi = share_of(start + nb - 1, T, G);
   if (g_lo == g_hi) return;                            // written directly by the partition kernel
   const int ns = g_hi - g_lo + 1;
-  // piece k lives in share g_lo + k: slot 0 (the unit is that share's first unit) except for the
-  // first piece when the unit began inside share g_lo's range after another unit. Empty shares
-  // (when there are fewer chunk groups than shares) hold no piece and are skipped.
-  const int slot_lo = (share_start(g_lo, T, G) == start) ? 0 : 1;
+  // piece k lives in share g_lo + k: slot 0 (the unit is that share's first unit with a chunk)
+  // except for the first piece when share g_lo began before the unit's places, where it holds the
+  // last chunk of an earlier unit first. Empty shares (when there are fewer place groups than
+  // shares) hold no piece and are skipped.
+  const int slot_lo = (share_start(g_lo, T, G) >= ustart) ? 0 : 1;
   const int dq = tid % DQ, grp = tid / DQ;
   float M = kNegInf, S = 0.f;
   f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
-  // FULL: every share holds at least one group of 4 chunks (at least as many groups as shares),
+  // FULL: every share holds at least one group of 4 places (at least as many groups as shares),
   // so no piece needs the 64-bit divisions of the emptiness test; the choice is uniform.
   auto fold = [&](auto full_c) {
     constexpr bool FULL = decltype(full_c)::value;

@@ -145,9 +145,11 @@ attn_status attn_prefill_varlen_fp8(const void* q, const void* k, const void* v,
  * Number of partitions (partition workgroups) a paged decode call will use
  * (split-KV, "Attention kernels", section "Prefill and decode attention").
  * The batch's work -- every (request, kv head, chunk of keys) -- is cut into
- * that many equal contiguous shares, so each partition streams the same number
- * of KV bytes whatever the mix of context lengths; a request whose keys span
- * several shares is merged from their partial results. requested > 0 is
+ * that many contiguous shares of equal planned cost: a chunk counts one, and a
+ * (request, kv head) of fewer than 256 chunks counts two more for starting it,
+ * so each partition takes about the same time whatever the mix of context
+ * lengths; a request whose keys span several shares is merged from their
+ * partial results. requested > 0 is
  * returned clamped to the useful count (at most one share per 4 chunks of the
  * largest possible batch) and to 4096; requested == 0 picks one partition per
  * resident workgroup slot of the device (compute units x workgroups per unit
