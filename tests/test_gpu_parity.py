@@ -132,6 +132,24 @@ def test_decode_fp8(gpu, d, bs):
         compare(out, lse, ref_o, ref_l, beyond_rounding=True, label=f"fp8 d={d} bs={bs} splits={splits}")
 
 
+@pytest.mark.parametrize("d,kv_format", [(128, "bf16"), (256, "e4m3fn")])
+def test_decode_planned_shares(gpu, d, kv_format):
+    """The share plan charges (request, kv head) units of fewer than 256 chunks two extra places
+    for starting a piece. Units at 254-257 chunks sit on both sides of that threshold, short units
+    between them, and partition counts up to one share per 4 places make shares that hold only a
+    unit's extra places (no piece of it) next to shares that start inside one."""
+    ch = 64 if d == 128 else 32                      # tokens per chunk of the decode kernel
+    lens = [1, 254 * ch, 2, 255 * ch, 255 * ch + 1, 65, 257 * ch, 3 * ch, 130]
+    gen = torch.Generator().manual_seed(77 + d)
+    case = _to(synth.make_paged(77 + d, lens, [1] * len(lens), 8, 2, d, 16, kv_format=kv_format,
+                                lengths_drawn=gen), gpu)
+    ref_o, ref_l = oracle_paged(case)
+    for splits in (0, 5, 200, 1000):
+        out, lse = _run_decode(case, splits)
+        compare(out, lse, ref_o, ref_l, beyond_rounding=kv_format == "e4m3fn",
+                label=f"planned shares d={d} {kv_format} splits={splits}")
+
+
 @pytest.mark.parametrize("g", [1, 2, 4, 8, 16])
 def test_decode_group_sizes_and_edges(gpu, g):
     lens = [0, 1, 2, 63, 64, 65, 257, 1000]
