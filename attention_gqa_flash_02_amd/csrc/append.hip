@@ -17,10 +17,12 @@
 //     the 16 bf16 values of each of its items into one 16-byte fp8 store (or stores them as two
 //     16-byte bf16 pieces).
 //   * V: the rows go to LDS and are written column-wise, the page being [D][bs] (tokens innermost).
-//     A 16-slot chunk of a page whose 16 slots are all new rows of this workgroup (same request) is
-//     written whole: (chunk, head_dim pair) items, one 16-byte piece per d row (two for a bf16
-//     cache). Every other row (the first and last rows of a request, a decode token, a chunk cut by
-//     the workgroup boundary) is written element by element, so that no slot outside the new rows
+//     A 16-slot chunk of a page whose 16 slots are all new rows of one request is written whole:
+//     (chunk, head_dim pair) items, one 16-byte piece per d row (two for a bf16 cache). A chunk cut
+//     by the boundary between two workgroups is written whole by the first of them, which reads
+//     the rows past its range from the new V rows directly; the second one leaves those rows out.
+//     Every other row (the first and last rows of a request that share a chunk with cached
+//     tokens, a decode token) is written element by element, so that no slot outside the new rows
 //     is touched.
 #include <type_traits>
 
@@ -92,7 +94,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   __shared__ long long s_page[kAppendRows];    // (block, head) page index of each row
   __shared__ int s_full[kAppendRows];          // first row of each whole 16-slot chunk
   __shared__ int s_prow[kAppendRows];          // the rows outside whole chunks
-  __shared__ int s_cnt[2];
+  __shared__ int s_cnt[4];         // whole chunks, other rows, rows left to the previous workgroup,
+                                   // first row of the chunk finished past the range (or -1)
   __shared__ __align__(16) bf16 s_v[kAppendRows * VS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -158,6 +161,21 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
     s_req[tid] = b;
     s_pos[tid] = pos;
     s_page[tid] = (long long)blk * p.Hkv + h;
+    // The 16-slot chunk across the boundary before global row x (a row of request [c0, c1) at
+    // position px) is written whole by the workgroup before the boundary when the boundary cuts it
+    // (px not a chunk start, row x - 1 of the same request) and all its 16 slots are new rows of
+    // the request. Both workgroups take the same decision from the same numbers.
+    auto cut_whole = [&](int x, int px) {
+      const int cs = x - (px & 15);                       // global row of the chunk's first slot
+      return (px & 15) != 0 && c0 < x && cs >= c0 && cs + 15 < c1;
+    };
+    if (tid == 0) s_cnt[2] = cut_whole(row, pos) ? 16 - (pos & 15) : 0;
+    if (tid == nrows - 1) {
+      // the boundary after this workgroup: row + 1 (only with a full range; a shorter one is the
+      // grid's last workgroup)
+      const int x = row + 1;
+      s_cnt[3] = (nrows == kAppendRows && x < c1 && cut_whole(x, pos + 1)) ? tid + 1 - ((pos + 1) & 15) : -1;
+    }
   }
   // ---- V rows into LDS
 #pragma unroll
@@ -172,22 +190,26 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   __syncthreads();
   // a row lies in a whole chunk when the 16 rows of its 16-slot chunk are all new rows of this
   // workgroup and of its request (then their positions are consecutive and fill the chunk)
+  // Rows below `head` belong to a cut chunk the previous workgroup writes; rows from `tail` on to a
+  // cut chunk this one finishes past its range.
+  const int head = s_cnt[2], tail = s_cnt[3];
   bool whole = false, whole_start = false;
   if (tid < nrows) {
     const int i0 = tid - (s_pos[tid] & 15);
     whole = i0 >= 0 && i0 + 15 < nrows && s_req[i0] == s_req[tid] && s_req[i0 + 15] == s_req[tid];
     whole_start = whole && i0 == tid;
   }
+  const bool other = tid < nrows && !whole && tid >= head && !(tail >= 0 && tid >= tail);
   // compact the whole-chunk starts and the other rows (the rows are held by wave 0)
   const uint64_t mw = __builtin_amdgcn_ballot_w64(whole_start);
-  const uint64_t mp = __builtin_amdgcn_ballot_w64(tid < nrows && !whole);
+  const uint64_t mp = __builtin_amdgcn_ballot_w64(other);
   if (tid == 0) {
     s_cnt[0] = __builtin_popcountll(mw);
     s_cnt[1] = __builtin_popcountll(mp);
   }
   if (whole_start)
     s_full[__builtin_amdgcn_mbcnt_hi((uint32_t)(mw >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mw, 0))] = tid;
-  if (tid < nrows && !whole)
+  if (other)
     s_prow[__builtin_amdgcn_mbcnt_hi((uint32_t)(mp >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mp, 0))] = tid;
   __syncthreads();
   const int nfull = s_cnt[0];
@@ -221,12 +243,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
       }
     }
 
-    // ---- V, whole chunks: (chunk, head_dim pair) items
-    for (int it = tid; it < nfull * HD; it += 256) {
-      const int i0 = s_full[it / HD], d = 2 * (it % HD);
-      uint32_t w[16];                                           // bf16 pairs (d, d + 1) of the 16 rows
-#pragma unroll
-      for (int t = 0; t < 16; ++t) w[t] = *reinterpret_cast<const uint32_t*>(s_v + (i0 + t) * VS + d);
+    // ---- V, whole chunks: (chunk, head_dim pair) items. w: bf16 pairs (d, d + 1) of the 16 rows;
+    // i0: the chunk's first row in this workgroup
+    auto write_chunk = [&](int i0, int d, const uint32_t (&w)[16]) {
       const size_t e0 = ((size_t)s_page[i0] * D + d) * p.bs + (s_pos[i0] & (p.bs - 1));   // (d, first slot)
       if constexpr (!FP8) {
         bf16* v0 = reinterpret_cast<bf16*>(p.v_cache) + e0;
@@ -253,6 +272,29 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
         }
         *reinterpret_cast<u32x4*>(v0) = u32x4{q0[0], q0[1], q0[2], q0[3]};
         *reinterpret_cast<u32x4*>(v0 + p.bs) = u32x4{q1[0], q1[1], q1[2], q1[3]};
+      }
+    };
+    for (int it = tid; it < nfull * HD; it += 256) {
+      const int i0 = s_full[it / HD], d = 2 * (it % HD);
+      uint32_t w[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) w[t] = *reinterpret_cast<const uint32_t*>(s_v + (i0 + t) * VS + d);
+      write_chunk(i0, d, w);
+    }
+    // ---- V, the chunk cut by the end of the range: its rows past the range come from the new
+    // rows in memory
+    if (tail >= 0) {
+      for (int d2 = tid; d2 < HD; d2 += 256) {
+        const int d = 2 * d2;
+        uint32_t w[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int r = tail + t;
+          w[t] = r < kAppendRows
+                     ? *reinterpret_cast<const uint32_t*>(s_v + r * VS + d)
+                     : *reinterpret_cast<const uint32_t*>(vnew + (size_t)(row0 + r) * row_stride + (size_t)h * D + d);
+        }
+        write_chunk(tail, d, w);
       }
     }
 

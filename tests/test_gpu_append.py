@@ -51,6 +51,19 @@ def test_append_mixed_batch(gpu, kv_format, d, bs, hkv):
     _check(case, gpu)
 
 
+@pytest.mark.parametrize("kv_format", ["bf16", "e4m3fn"])
+@pytest.mark.parametrize("d,bs", [(128, 16), (256, 16), (128, 32), (256, 64), (128, 256)])
+def test_append_chunks_cut_by_workgroups(gpu, kv_format, d, bs):
+    """Long runs of new rows at every alignment to the 16-slot chunks of a page, so that the
+    64-row ranges of the workgroups cut chunks inside a request (written whole by the first
+    workgroup, partly from rows past its range), start or end a request inside a cut chunk, and
+    end the batch in a short last range."""
+    prior = [5, 16, 37, 0, 250, 1, 15, 94]
+    new = [300, 200, 129, 64, 77, 63, 1, 95]
+    case = synth.make_append(400 + d + bs, prior, new, 2, d, bs, kv_format, value_std=2.0)
+    _check(case, gpu)
+
+
 def test_append_many_requests_and_rounding_ties(gpu):
     # 700 requests (the row -> request search crosses its LDS window), mostly single tokens with
     # runs of empty requests; one head's scale is 1 so that quotients hit e4m3 midpoints exactly
