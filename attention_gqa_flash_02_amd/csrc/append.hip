@@ -8,11 +8,12 @@
 // stores e4m3fn(x / scale[h]): the quotient in correctly rounded fp32, clamped to +-448, converted
 // with round-to-nearest-even.
 //
-// Work layout: a workgroup takes 64 consecutive new-token rows of one kv head. Its threads first
-// load those rows' K and V (32 contiguous bytes per thread and item: these loads do not depend on
-// where the rows land, so they are in flight while the rows' requests are found: a coarse sample of
-// cu_seqlens_new, then, for more than 255 requests, the window that holds the first row, and a
-// search in LDS) and their cache slots. Then:
+// Work layout: a workgroup takes 64 consecutive new-token rows of one kv head. Waves 1-3 load
+// those rows' K and V (32 contiguous bytes per thread and item); these loads do not depend on where
+// the rows land. Wave 0 meanwhile finds each row's request (a coarse sample of cu_seqlens_new, then,
+// for more than 255 requests, the window that holds the first row, and a search in LDS) and cache
+// slot; it loads no K or V itself, since a wave's loads return in order and its three dependent
+// lookups would otherwise wait behind them. Then:
 //   * K: every row's K row is one contiguous byte range of its page ([bs][D]); each thread converts
 //     the 16 bf16 values of each of its items into one 16-byte fp8 store (or stores them as two
 //     16-byte bf16 pieces).
@@ -84,10 +85,12 @@ template <int D, bool FP8>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   constexpr int ELT = FP8 ? 1 : 2;
   constexpr int IPR = D / 16;                  // 32-byte source items (16 bf16 values) per row
-  constexpr int ITEMS = kAppendRows * IPR / 256;   // items per thread
+  constexpr int NITEM = kAppendRows * IPR;     // items of a workgroup
+  constexpr int LT = 192;                      // loading threads: waves 1-3 (wave 0 finds the slots)
+  constexpr int ITEMS = (NITEM + LT - 1) / LT; // items per loading thread
   constexpr int HD = D / 2;                    // head_dim pairs
   constexpr int VS = D + 2;                    // LDS row stride of the staged V rows (bf16)
-  static_assert(kAppendRows * IPR % 256 == 0, "whole items per thread");
+  static_assert(kAppendRows == 64, "wave 0 holds one row per lane");
   __shared__ int s_cu[257];
   __shared__ int s_req[kAppendRows];           // request of each row
   __shared__ int s_pos[kAppendRows];           // cache position of each row
@@ -105,26 +108,34 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   const int B = p.num_seqs;
   const size_t row_stride = (size_t)p.Hkv * D;              // elements between consecutive new rows
 
-  // ---- the rows' K and V into registers: item i = tid + 256 u is row i / IPR, values 16 (i % IPR) ..
+  // ---- the rows' K and V into the registers of waves 1-3: item i = lt + 192 u is row i / IPR,
+  // values 16 (i % IPR) .. + 15. Wave 0 loads none: a wave's loads return in order, so its search
+  // below (three dependent loads) does not wait behind them.
   const bf16* __restrict__ knew = p.k_new;
   const bf16* __restrict__ vnew = p.v_new;
+  const int lt = tid - 64;                     // loading thread, negative in wave 0
   u32x4 kin[ITEMS][2], vin[ITEMS][2];
+  if (lt >= 0) {
 #pragma unroll
-  for (int u = 0; u < ITEMS; ++u) {
-    const int i = tid + 256 * u, r = min(i / IPR, nrows - 1), c = i % IPR;
-    const size_t off = (size_t)(row0 + r) * row_stride + (size_t)h * D + 16 * c;
+    for (int u = 0; u < ITEMS; ++u) {
+      const int i = min(lt + LT * u, NITEM - 1), r = min(i / IPR, nrows - 1), c = i % IPR;
+      const size_t off = (size_t)(row0 + r) * row_stride + (size_t)h * D + 16 * c;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      kin[u][q] = *reinterpret_cast<const u32x4*>(knew + off + 8 * q);
-      vin[u][q] = *reinterpret_cast<const u32x4*>(vnew + off + 8 * q);
+      for (int q = 0; q < 2; ++q) {
+        kin[u][q] = *reinterpret_cast<const u32x4*>(knew + off + 8 * q);
+        vin[u][q] = *reinterpret_cast<const u32x4*>(vnew + off + 8 * q);
+      }
     }
   }
 
   // ---- requests of the rows: coarse sample, then the window holding the first row (one round
   // when the whole cu_seqlens_new fits the sample)
   const int step = (B + 256) / 256;            // ceil((B + 1) / 256) requests per sample
-  s_cu[tid] = p.cu_seqlens_new[min(tid * step, B)];
-  if (tid == 0) s_cu[256] = p.cu_seqlens_new[B];
+  if (tid < 64) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s_cu[tid + 64 * k] = p.cu_seqlens_new[min((tid + 64 * k) * step, B)];
+    if (tid == 0) s_cu[256] = p.cu_seqlens_new[B];
+  }
   __syncthreads();
   int base = 0;
   if (step > 1) {
@@ -135,8 +146,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
     }
     base = lo * step;
     __syncthreads();
-    s_cu[tid] = p.cu_seqlens_new[min(base + tid, B)];
-    if (tid == 0) s_cu[256] = p.cu_seqlens_new[min(base + 256, B)];
+    if (tid < 64) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s_cu[tid + 64 * k] = p.cu_seqlens_new[min(base + tid + 64 * k, B)];
+      if (tid == 0) s_cu[256] = p.cu_seqlens_new[min(base + 256, B)];
+    }
     __syncthreads();
   }
   if (tid < nrows) {
@@ -178,14 +192,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
     }
   }
   // ---- V rows into LDS
+  if (lt >= 0) {
 #pragma unroll
-  for (int u = 0; u < ITEMS; ++u) {
-    const int i = tid + 256 * u, r = i / IPR, c = i % IPR;
-    bf16* dst = s_v + r * VS + 16 * c;
+    for (int u = 0; u < ITEMS; ++u) {
+      const int i = lt + LT * u, r = i / IPR, c = i % IPR;
+      if (i >= NITEM) break;
+      bf16* dst = s_v + r * VS + 16 * c;
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) *reinterpret_cast<uint32_t*>(dst + 8 * q + 2 * w) = vin[u][q][w];
+        for (int w = 0; w < 4; ++w) *reinterpret_cast<uint32_t*>(dst + 8 * q + 2 * w) = vin[u][q][w];
+    }
   }
   __syncthreads();
   // a row lies in a whole chunk when the 16 rows of its 16-slot chunk are all new rows of this
@@ -225,8 +242,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
     // ---- K: each item (16 values of one row) becomes one 16-byte fp8 piece or two bf16 pieces
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u) {
-      const int i = tid + 256 * u, r = i / IPR, c = i % IPR;
-      if (r >= nrows) continue;
+      const int i = lt + LT * u, r = i / IPR, c = i % IPR;
+      if (lt < 0 || i >= NITEM || r >= nrows) continue;
       char* dst = reinterpret_cast<char*>(p.k_cache) +
                   (((size_t)s_page[r] * p.bs + (s_pos[r] & (p.bs - 1))) * D + 16 * c) * ELT;
       if constexpr (!FP8) {
