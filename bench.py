@@ -280,10 +280,7 @@ def append_section(lib, steps, warmup):
     bf16 K and V read once, their fp8 codes written once."""
     import torch
     import synth
-    g = torch.Generator().manual_seed(5)
-    prior = [int(x) for x in torch.randint(0, 32769, (8,), generator=g)] + \
-            [int(x) - 1 for x in torch.randint(512, 32769, (120,), generator=g)]
-    new = [2048] * 8 + [1] * 120
+    prior, new = synth.mixed_step_append_lengths()
     case = synth.make_append(5, prior, new, 4, 256, 16, "e4m3fn", cache_content=False)
     dev = torch.device("cuda:0")
     pool = int(case.block_table.max()) + 1

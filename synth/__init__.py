@@ -35,6 +35,7 @@ from .cases import (
     make_paged,
     AppendCase,
     make_append,
+    mixed_step_append_lengths,
     CONFIGS,
     config_case,
 )
@@ -46,6 +47,7 @@ __all__ = [
     "make_prefill_fp8",
     "AppendCase",
     "make_append",
+    "mixed_step_append_lengths",
     "make_prefill",
     "make_paged",
     "CONFIGS",

@@ -306,8 +306,18 @@ class AppendCase:
     kv_format: str
 
 
+def mixed_step_append_lengths():
+    """Cached and new token counts of the KV-cache append of one mixed step: 8 prefill chunks of
+    2048 new tokens over prefixes U[0, 32768] and 120 decode tokens over contexts U[512, 32768]
+    (seed 5). Returns (prior_lens, new_lens)."""
+    g = torch.Generator().manual_seed(5)
+    prior = [int(x) for x in torch.randint(0, 32769, (8,), generator=g)] + \
+            [int(x) - 1 for x in torch.randint(512, 32769, (120,), generator=g)]
+    return prior, [2048] * 8 + [1] * 120
+
+
 def make_append(seed, prior_lens, new_lens, num_kv_heads, head_dim, block_size, kv_format="bf16",
-                value_std=1.0, scales=None, cache_content=True):
+                value_std=1.0, scales=None, cache_content=True, shared_prior_page=False):
     """Seeded append case. Draw order: page permutation -> prior cache content -> K_new -> V_new.
 
     The cache pool holds every request's blocks (prior + new tokens) plus spare blocks, in
@@ -316,19 +326,35 @@ def make_append(seed, prior_lens, new_lens, num_kv_heads, head_dim, block_size, 
     values spread over [0.002, 0.05] (so that some quotients saturate and some are subnormal).
     With cache_content=False the caches are left as None (the pool size is
     block_table.max() + 1 or more) and no prior content is drawn.
+    With shared_prior_page=True only the blocks that receive new tokens get pages of their own
+    (pages 1 .. in randperm order); every other logical block maps to page 0, which the append must
+    leave unchanged. This keeps the pool small for long cached prefixes.
     """
     g = torch.Generator().manual_seed(seed)
     lens = [p + n for p, n in zip(prior_lens, new_lens)]
     nblocks = [max(1, -(-L // block_size)) for L in lens]
-    spare = max(2, sum(nblocks) // 20)
-    pool = sum(nblocks) + spare
-    perm = torch.randperm(pool, generator=g)
     max_blocks = max(nblocks)
     table = torch.zeros((len(lens), max_blocks), dtype=torch.int32)
-    used = 0
-    for b, nb in enumerate(nblocks):
-        table[b, :nb] = perm[used:used + nb].to(torch.int32)
-        used += nb
+    if shared_prior_page:
+        touched = [range(p // block_size, (p + n - 1) // block_size + 1) if n > 0 else range(0)
+                   for p, n in zip(prior_lens, new_lens)]
+        count = sum(len(r) for r in touched)
+        spare = max(2, count // 20)
+        pool = 1 + count + spare
+        perm = 1 + torch.randperm(pool - 1, generator=g)
+        used = 0
+        for b, r in enumerate(touched):
+            for lb in r:
+                table[b, lb] = int(perm[used])
+                used += 1
+    else:
+        spare = max(2, sum(nblocks) // 20)
+        pool = sum(nblocks) + spare
+        perm = torch.randperm(pool, generator=g)
+        used = 0
+        for b, nb in enumerate(nblocks):
+            table[b, :nb] = perm[used:used + nb].to(torch.int32)
+            used += nb
     fp8 = kv_format != "bf16"
     if not cache_content:                    # timing only: the caller allocates the pool
         k_cache = v_cache = None

@@ -64,6 +64,17 @@ def test_append_chunks_cut_by_workgroups(gpu, kv_format, d, bs):
     _check(case, gpu)
 
 
+def test_append_mixed_step_full(gpu):
+    """The append the bench times, at full size and in its launch configuration: the new tokens of
+    one mixed step (8 prefill chunks of 2048 over prefixes U[0, 32768] and 120 decodes over
+    contexts U[512, 32768]), 4 KV heads, head_dim 256, 16-token pages, e4m3fn codes. Only the
+    pages that receive new tokens are distinct; every cached-only block shares page 0, which must
+    stay unchanged like every other byte."""
+    prior, new = synth.mixed_step_append_lengths()
+    case = synth.make_append(5, prior, new, 4, 256, 16, "e4m3fn", shared_prior_page=True)
+    _check(case, gpu)
+
+
 def test_append_many_requests_and_rounding_ties(gpu):
     # 700 requests (the row -> request search crosses its LDS window), mostly single tokens with
     # runs of empty requests; one head's scale is 1 so that quotients hit e4m3 midpoints exactly
