@@ -33,6 +33,18 @@ def test_prefill_window(gpu, window, causal, d, hq, hkv):
     compare(out, lse, ref_o, ref_l, label=f"prefill window={window} causal={causal} d={d} hq={hq} hkv={hkv}")
 
 
+def test_prefill_window_4x8192_full(gpu):
+    """The windowed prefill the bench times: causal 4 x 8192, 32/8 heads, head_dim 128, a 4096-key
+    window, checked on sampled (sequence, head) units; rows past 4096 see exactly 4096 keys."""
+    case = _to(synth.config_case("c3"), gpu)
+    out, lse = lib.attn_prefill_varlen(case.q, case.k, case.v, case.cu_seqlens, case.causal, case.scale,
+                                       max_seqlen=case.max_seqlen, window=4096)
+    torch.cuda.synchronize()
+    units = [(0, 3), (1, 12), (2, 21), (3, 29)]
+    ref_o, ref_l = oracle_prefill(case, units=units, window=4096)
+    compare(out, lse, ref_o, ref_l, label="prefill 4x8192 window=4096 full (4 units)")
+
+
 @pytest.mark.parametrize("window", [1, 100, 1000, 5000])
 @pytest.mark.parametrize("splits", [0, 3, 16])
 def test_decode_window(gpu, window, splits):
