@@ -54,6 +54,27 @@ def test_prefill_4x8192_full(gpu):
     compare(out, lse, ref_o, ref_l, label="prefill 4x8192 full (4 units)")
 
 
+@pytest.mark.parametrize("q_len", [4, 8])
+def test_multi_token_decode_batch32_full(gpu, q_len):
+    """Speculative verification on the batch-32 decode cache, as the bench times it: each request's
+    last q_len cached tokens are new query rows (causal), 32/8 heads, so 16 or 32 rows per KV head
+    take the split-KV decode path in one or two 16-row blocks, with the library's partition count;
+    checked on sampled (request, head) units."""
+    case = _to(synth.config_case("c2"), gpu)
+    b, hq, d = case.q.shape
+    g = torch.Generator().manual_seed(21)
+    case.q = torch.randn((b * q_len, hq, d), generator=g).to(torch.bfloat16).to(gpu)
+    case.cu_seqlens_q = torch.arange(0, b * q_len + 1, q_len, dtype=torch.int32, device=gpu)
+    case.causal = True
+    s = lib.attn_decode_num_splits(b, case.num_kv_heads, d, 0, case.block_size, case.block_table.shape[1], 0)
+    out, lse = lib.attn_varlen_paged(case.q, case.k_cache, case.v_cache, case.block_table, case.cu_seqlens_q,
+                                     case.seq_lens_k, True, case.scale, max_q_len=q_len, num_splits=s)
+    torch.cuda.synchronize()
+    units = [(0, 0), (9, 6), (17, 13), (25, 22), (31, 31)]
+    ref_o, ref_l = oracle_paged(case, units=units)
+    compare(out, lse, ref_o, ref_l, label=f"multi-token q_len={q_len} batch-32 full (5 units)")
+
+
 @pytest.mark.parametrize("splits", [16, 64, 0])
 def test_splitkv_2x131072_full(gpu, splits):
     """2 requests of 131072 cached tokens, 32/2 heads (group 16), 64-token pages: the partition
