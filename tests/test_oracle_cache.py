@@ -136,3 +136,32 @@ def test_append_then_gather_returns_the_tokens_and_chunks_compose(kv_format):
     sel = np.r_[0:3, 15:23, 23:24]
     kcb, vcb = oracle.kv_append_paged(kca, vca, k_new[sel], v_new[sel], table, cu_b, np.array(lens), **kw)
     assert np.array_equal(kcb, kc2) and np.array_equal(vcb, vc2)
+
+
+def test_synth_append_shared_prior_page():
+    """The compact append case used at full size: blocks that receive new tokens get distinct
+    pages 1 ..; every other logical block maps to page 0, which the oracle's scatter never writes
+    (so a kernel write there shows up in the byte comparison)."""
+    import synth
+    prior, new = [0, 5, 16, 100, 7, 31, 250], [1, 3, 17, 64, 0, 1, 45]
+    case = synth.make_append(9, prior, new, 2, 128, 16, "e4m3fn", shared_prior_page=True)
+    table = case.block_table.numpy()
+    pages = []
+    for b, (p, n) in enumerate(zip(prior, new)):
+        touched = set(range(p // 16, (p + n - 1) // 16 + 1)) if n else set()
+        for lb in range(-(-(p + n) // 16)):
+            if lb in touched:
+                assert table[b, lb] >= 1
+                pages.append(int(table[b, lb]))
+            else:
+                assert table[b, lb] == 0
+    assert len(pages) == len(set(pages)) and max(pages) < case.k_cache.shape[0]
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 \
+            else t.contiguous().view(torch.uint8).numpy()
+    kc, vc = oracle.kv_append_paged(bits(case.k_cache), bits(case.v_cache), bits(case.k_new), bits(case.v_new),
+                                    table, case.cu_seqlens_new.numpy(), case.seq_lens_k.numpy(), kv_format="e4m3fn",
+                                    k_scale=case.k_scale.numpy(), v_scale=case.v_scale.numpy())
+    assert np.array_equal(kc[0], bits(case.k_cache)[0]) and np.array_equal(vc[0], bits(case.v_cache)[0])
+    assert not np.array_equal(kc[pages], bits(case.k_cache)[pages])
