@@ -91,6 +91,17 @@ def test_append_many_requests_and_rounding_ties(gpu):
     _check(case, gpu)
 
 
+@pytest.mark.parametrize("kv_format", ["bf16", "e4m3fn"])
+def test_append_rows_past_the_search_window(gpu, kv_format):
+    """1000 requests with 600 empty ones after the first: the first workgroup's rows 3 .. belong to
+    requests 601 .., outside the 257-entry window of cu_seqlens_new it holds in LDS (requests
+    0 .. 256), so their requests are found by the search in memory."""
+    new = [3] + [0] * 600 + [2] + [1] * 398
+    prior = [5 + (7 * b) % 40 for b in range(len(new))]
+    case = synth.make_append(91, prior, new, 2, 128, 16, kv_format, value_std=2.0)
+    _check(case, gpu)
+
+
 def test_append_empty_is_a_noop(gpu):
     case = synth.make_append(3, [4, 9], [0, 0], 2, 128, 16, "bf16")
     _check(case, gpu)
