@@ -150,6 +150,21 @@ def test_decode_planned_shares(gpu, d, kv_format):
                 label=f"planned shares d={d} {kv_format} splits={splits}")
 
 
+@pytest.mark.parametrize("d,kv_format", [(128, "bf16"), (256, "e4m3fn")])
+def test_decode_many_requests(gpu, d, kv_format):
+    """600 requests (more than the 256 threads of the plan's prefix, so each sums several), a
+    tenth of them empty, lengths up to 300: the plan, the shares and the merge over many short
+    units, at the library's partition count and at a few others."""
+    g = np.random.default_rng(600 + d)
+    lens = [0 if x < 0.1 else int(y) for x, y in zip(g.random(600), g.integers(1, 301, 600))]
+    case = _to(synth.make_paged(600 + d, lens, [1] * len(lens), 8, 2, d, 16, kv_format=kv_format), gpu)
+    ref_o, ref_l = oracle_paged(case)
+    for splits in (0, 7, 300, 2000):
+        out, lse = _run_decode(case, splits)
+        compare(out, lse, ref_o, ref_l, beyond_rounding=kv_format == "e4m3fn",
+                label=f"600 requests d={d} {kv_format} splits={splits}")
+
+
 @pytest.mark.parametrize("g", [1, 2, 4, 8, 16])
 def test_decode_group_sizes_and_edges(gpu, g):
     lens = [0, 1, 2, 63, 64, 65, 257, 1000]
@@ -173,6 +188,19 @@ def _run_varlen(case, splits=0):
                                      v_scale=case.v_scale, num_splits=splits)
     torch.cuda.synchronize()
     return out, lse
+
+
+def test_varlen_many_requests(gpu):
+    """300 requests in one mixed call: mostly single decode tokens, some multi-token requests and
+    prefill chunks of up to 100 rows over cached prefixes, and empty caches."""
+    g = np.random.default_rng(300)
+    q_lens = [int(x) for x in g.choice([1, 1, 1, 1, 2, 4, 33, 100], size=300)]
+    kv_lens = [q + int(p) for q, p in zip(q_lens, g.integers(0, 400, 300))]
+    case = _to(synth.make_paged(301, kv_lens, q_lens, 8, 2, 128, 16), gpu)
+    ref_o, ref_l = oracle_paged(case)
+    for splits in (0, 5):
+        out, lse = _run_varlen(case, splits)
+        compare(out, lse, ref_o, ref_l, label=f"300 requests mixed splits={splits}")
 
 
 def test_varlen_c5_shrunk(gpu):
