@@ -2,6 +2,7 @@
 oracle of the decoded inputs: ragged varlen batches, causal and not, sliding windows, group sizes
 1-8, the 4 x 8192 workload on sampled (request, head) units, and the edge cases."""
 
+import numpy as np
 import pytest
 import torch
 
@@ -64,6 +65,18 @@ def test_fp8_prefill_long_sampled(gpu):
     units = [(0, 0), (1, 7), (2, 19), (3, 31)]
     ref_o, ref_l = oracle_prefill_fp8(case, units=units)
     compare(out, lse, ref_o, ref_l, max_abs=MAX_ABS_FP8, mean_abs=MEAN_ABS_FP8, label="fp8 prefill 4x8192 sampled")
+
+
+def test_fp8_prefill_many_sequences(gpu):
+    """800 short sequences (1 to 40 tokens, a few of 300) in one fp8 call."""
+    g = np.random.default_rng(880)
+    lens = [int(x) for x in g.integers(1, 41, 800)]
+    for i in (3, 500, 799):
+        lens[i] = 300
+    case = _to(synth.make_prefill_fp8(880, lens, 8, 2, 128), gpu)
+    out, lse = _run(case)
+    ref_o, ref_l = oracle_prefill_fp8(case)
+    compare(out, lse, ref_o, ref_l, max_abs=MAX_ABS_FP8, mean_abs=MEAN_ABS_FP8, label="fp8 prefill 800 sequences")
 
 
 def test_fp8_prefill_edges(gpu):
