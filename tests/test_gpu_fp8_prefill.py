@@ -29,7 +29,7 @@ def _run(case, window=0):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4), (8, 4), (16, 2), (6, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4), (8, 4), (16, 2), (6, 2), (32, 2)])
 def test_fp8_prefill_ragged(gpu, causal, hq, hkv):
     lens = [1, 17, 64, 65, 200, 1000, 31]
     case = _to(synth.make_prefill_fp8(900 + hq * 10 + hkv, lens, hq, hkv, 128, causal=causal), gpu)

@@ -59,7 +59,7 @@ def test_prefill_c3_shrunk(gpu):
     compare(out, lse, ref_o, ref_l, label="c3/16")
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (6, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (6, 2), (32, 2)])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("d", [128, 256])
 def test_prefill_varlen_ragged(gpu, hq, hkv, causal, d):
