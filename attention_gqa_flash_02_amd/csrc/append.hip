@@ -103,7 +103,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int h = blockIdx.y;
-  const int row0 = blockIdx.x * kAppendRows;
+  // row blocks from the last one: a batch's single-token (decode) rows usually come last, and
+  // their scattered V columns make theirs the slowest workgroups, so they start first
+  const int row0 = ((int)gridDim.x - 1 - (int)blockIdx.x) * kAppendRows;
   const int nrows = min(kAppendRows, p.total_new - row0);
   const int B = p.num_seqs;
   const size_t row_stride = (size_t)p.Hkv * D;              // elements between consecutive new rows
