@@ -92,6 +92,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   constexpr int VS = D + 2;                    // LDS row stride of the staged V rows (bf16)
   static_assert(kAppendRows == 64, "wave 0 holds one row per lane");
   __shared__ int s_cu[257];
+  __shared__ int s_sl[256];                    // seq_lens_k, with at most 255 requests
   __shared__ int s_req[kAppendRows];           // request of each row
   __shared__ int s_pos[kAppendRows];           // cache position of each row
   __shared__ long long s_page[kAppendRows];    // (block, head) page index of each row
@@ -137,6 +138,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) s_cu[tid + 64 * k] = p.cu_seqlens_new[min((tid + 64 * k) * step, B)];
     if (tid == 0) s_cu[256] = p.cu_seqlens_new[B];
+    if (step == 1) {                           // then seq_lens_k fits too: one lookup fewer below
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s_sl[tid + 64 * k] = p.seq_lens_k[min(tid + 64 * k, B - 1)];
+    }
   }
   __syncthreads();
   int base = 0;
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
       c0 = p.cu_seqlens_new[b];
       c1 = p.cu_seqlens_new[b + 1];
     }
-    const int pos = p.seq_lens_k[b] - (c1 - c0) + (row - c0);
+    const int pos = (step == 1 ? s_sl[b] : p.seq_lens_k[b]) - (c1 - c0) + (row - c0);
     const int blk = p.block_table[(size_t)b * p.max_blocks + pos / p.bs];
     s_req[tid] = b;
     s_pos[tid] = pos;
