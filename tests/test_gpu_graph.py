@@ -1,8 +1,8 @@
 """The paged decode, the mixed varlen call and the KV append (with the decode after it) inside a
-captured HIP graph: the library allocates
-nothing, never synchronises and records no memset, so a serving loop can capture a step once and
-replay it. Each replay runs on new query values written into the captured input buffer, with eager
-work in between, and must equal the eager call on the same inputs bit for bit."""
+captured HIP graph: the library allocates nothing, never synchronises and records no memset, so a
+serving loop can capture a step once and replay it. Each replay runs on new input values written
+into the captured buffers, with eager work in between, and must equal the eager call on the same
+inputs bit for bit."""
 
 import pytest
 import torch
