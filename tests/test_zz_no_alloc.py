@@ -2,7 +2,8 @@
 the library's fixed per-GPU array instead of a caller workspace) against attn_decode_paged on the
 same inputs, through the C ABI. The two share their kernels, so with the same partition count the
 outputs must be bit-identical. Two calls in a row, the second on a smaller batch (the array keeps the
-first call's contents), then a shape whose partials exceed the array (rejected before any launch).
+first call's contents), then a shape whose partials exceed the array (rejected before any launch),
+and the entry point captured in a graph and replayed with other no-alloc calls in between.
 Validation of the new entry point is also checked without a GPU."""
 
 import ctypes
@@ -98,3 +99,44 @@ def test_noalloc_rejects_oversized_partials(gpu):
                                                case.scale)
     torch.cuda.synchronize()
     assert torch.equal(out2, out_ref) and torch.equal(lse2, lse_ref)
+
+
+@pytest.mark.gpu
+def test_noalloc_in_graph(gpu):
+    """The callers the entry point is for: captured once in a graph and replayed. Between replays an
+    eager no-alloc call on another batch overwrites the shared array; every replay, on new query
+    values, must still equal attn_decode_paged on the same inputs bit for bit."""
+    case = _to(synth.config_case("c2", shrink=4), gpu)
+    other = _to(synth.make_paged(94, [2000, 9, 640], [1, 1, 1], 32, 8, 128, 16,
+                                 lengths_drawn=torch.Generator().manual_seed(94)), gpu)
+    b, hq, d = case.q.shape
+    out = torch.empty_like(case.q)
+    lse = torch.empty((b, hq), dtype=torch.float32, device=gpu)
+    splits = lib.attn_decode_num_splits(b, case.num_kv_heads, d, 0, case.block_size, case.block_table.shape[1], 0)
+
+    def call():
+        lib.attn_decode_paged_noalloc(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens_k,
+                                      case.scale, out=out, lse=lse, num_splits=splits)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cpu").manual_seed(95)
+    for rep in range(3):
+        lib.attn_decode_paged_noalloc(other.q, other.k_cache, other.v_cache, other.block_table, other.seq_lens_k,
+                                      other.scale, num_splits=7)
+        torch.cuda.synchronize()
+        case.q.copy_(torch.randn(case.q.shape, generator=gen).to(torch.bfloat16).to(gpu))
+        graph.replay()
+        torch.cuda.synchronize()
+        out_ref, lse_ref = lib.attn_decode_paged(case.q, case.k_cache, case.v_cache, case.block_table,
+                                                 case.seq_lens_k, case.scale, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_ref), f"replay {rep}: out differs"
+        assert torch.equal(lse, lse_ref), f"replay {rep}: lse differs"
